@@ -1,0 +1,115 @@
+"""Python access to the fp64 attention-forward oracle (``attn_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path. It loads the C
+oracle through ctypes and shares nothing with the HIP library.
+
+The computation is the plain definition of attention (PipeThreader OSDI'25
+summary page, "FlashAttention-3" paragraph: acc_s = Q K^T, softmax gives P,
+O = P V), with the readings for scale, causal mask and log-sum-exp stated in
+the C file's header.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def compile_source(src: str, out_path: str) -> str:
+    """Compile one oracle C source into a shared library at ``out_path``.
+
+    No ``-march=native`` and no fast-math: the library is built in one
+    container and run on another host, and IEEE semantics are required.
+    """
+    tmp = out_path + ".tmp"
+    cmd = ["gcc", "-O3", "-fopenmp", "-fno-fast-math", "-fPIC", "-shared", "-std=c11",
+           src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/liboracle.so`` (gcc + OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    return compile_source(_SRC, _LIB_PATH)
+
+
+SOURCE_PATH = _SRC
+
+
+def bind(path: str):
+    """Load a compiled oracle library from ``path`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_attn_fwd_rows.restype = ctypes.c_int
+    lib.oracle_attn_fwd_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = bind(_LIB_PATH)
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def attn_fwd_rows(q, k, v, causal: bool, scale, rows=None, threads: int = 0, lib=None):
+    """fp64 attention forward for selected rows.
+
+    q, k, v: uint16 bf16 bit arrays [B, H, N, d]. ``rows``: flat row ids
+    (b*H + h)*N + i, or None for every row. ``scale`` is converted to float32,
+    the exact value the GPU path receives.
+    Returns (out [n_rows, d] float64, lse [n_rows] float64).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if rows is None:
+        n_rows = B * H * N
+        rows_ptr = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.size
+        rows_ptr = rows.ctypes.data
+    out = np.empty((n_rows, d), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    rc = (lib or _load()).oracle_attn_fwd_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, int(bool(causal)),
+        float(np.float32(scale)), rows_ptr, n_rows, out.ctypes.data, lse.ctypes.data, int(threads))
+    if rc < 0:
+        raise ValueError("oracle rejected its arguments")
+    if rc > 0:
+        raise ArithmeticError(f"{rc} softmax rows failed the sum-to-one self-check")
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal: bool, scale, threads: int = 0, lib=None):
+    """fp64 attention forward over every row: (out [B,H,N,d], lse [B,H,N])."""
+    B, H, N, d = q.shape
+    out, lse = attn_fwd_rows(q, k, v, causal, scale, None, threads, lib)
+    return out.reshape(B, H, N, d), lse.reshape(B, H, N)

@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs for attention forward.
+
+This module only produces data: the workload shapes and bf16 Q/K/V tensors
+drawn from a seeded generator. It holds none of the attention arithmetic, so
+both the HIP path (through its tests and the benchmark) and the CPU oracle can
+consume the same inputs without sharing any of the method's code.
+
+Recipe (the pages give shapes only as "bf16 ~ N(0,1) from seed"):
+  * numpy ``default_rng(seed)`` (PCG64); Q, then K, then V are each drawn as
+    float32 ``standard_normal((B, H, N, d))`` from that one generator;
+  * each float32 is rounded to bf16 with round-to-nearest-even on its bit
+    pattern;
+  * the "max-tracking stress" variant multiplies every key row whose index is
+    a multiple of 7 by 8 after rounding (exact in bf16: an exponent shift);
+  * the scale handed to the kernel is the float32 value of 1/sqrt(d).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """One attention-forward workload: shapes, mask and the input recipe."""
+
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    seed: int
+    key_stress: bool = False  # every 7th key row multiplied by 8
+
+    @property
+    def scale(self) -> np.float32:
+        return default_scale(self.d)
+
+    def visible_pairs_per_head(self) -> int:
+        """Number of (query, key) pairs that take part in the softmax."""
+        n = self.N
+        return n * (n + 1) // 2 if self.causal else n * n
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: both contractions over the visible pairs only."""
+        return 4 * self.B * self.H * self.d * self.visible_pairs_per_head()
+
+
+# The five workloads, named by what they are.
+SMALL = AttnConfig("b1_h2_n256_d64", 1, 2, 256, 64, False, seed=1)
+CAUSAL_2K = AttnConfig("b4_h16_n2048_d128_causal", 4, 16, 2048, 128, True, seed=2)
+LONG_16K = AttnConfig("b2_h16_n16384_d128", 2, 16, 16384, 128, False, seed=3)
+CAUSAL_8K_STRESS = AttnConfig("b8_h32_n8192_d64_causal_keyx8", 8, 32, 8192, 64, True, seed=4,
+                              key_stress=True)
+CAUSAL_4K_D256 = AttnConfig("b2_h8_n4096_d256_causal", 2, 8, 4096, 256, True, seed=5)
+
+CONFIGS = [SMALL, CAUSAL_2K, LONG_16K, CAUSAL_8K_STRESS, CAUSAL_4K_D256]
+HEADLINE = LONG_16K
+
+
+def default_scale(d: int) -> np.float32:
+    """The float32 softmax scale 1/sqrt(d) passed to both sides."""
+    return np.float32(1.0 / np.sqrt(d))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits.
+
+    Inputs here are finite; NaN handling is not needed for the generator.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gen_qkv(B: int, H: int, N: int, d: int, seed: int, key_stress: bool = False):
+    """Return (q, k, v) as contiguous uint16 bf16 bit arrays of shape [B, H, N, d]."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    if key_stress:
+        kf = bf16_bits_to_f32(k)
+        kf[:, :, ::7, :] *= np.float32(8.0)
+        k = f32_to_bf16_bits(kf)
+    return q, k, v
+
+
+def gen_config(cfg: AttnConfig):
+    """Inputs of a named workload."""
+    return gen_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.key_stress)
+
+
+def sample_rows(B: int, H: int, N: int, per_head: int, seed: int, tile: int = 64) -> np.ndarray:
+    """Deterministic stratified sample of flat row ids in [0, B*H*N).
+
+    Every (b, h) gets rows 0 and N-1, rows on both sides of several tile
+    boundaries, and random rows; used where the oracle cannot run every row.
+    """
+    rng = np.random.default_rng(seed + 1000)
+    rows = []
+    for bh in range(B * H):
+        cand = {0, N - 1}
+        nt = (N + tile - 1) // tile
+        for t in rng.choice(nt, size=min(nt, 3), replace=False):
+            for off in (t * tile - 1, t * tile, t * tile + tile - 1):
+                if 0 <= off < N:
+                    cand.add(int(off))
+        rest = np.setdiff1d(np.arange(N), np.fromiter(cand, dtype=np.int64))
+        extra = min(rest.size, max(0, per_head - len(cand)))
+        cand.update(int(x) for x in rng.choice(rest, size=extra, replace=False))
+        rows.extend(bh * N + i for i in sorted(cand))
+    return np.asarray(sorted(set(rows)), dtype=np.int64)
