@@ -1,0 +1,98 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention-forward library
+ * (libattn.so). Plain C types only; no C++ or framework types cross it.
+ *
+ * The operation (PipeThreader, OSDI'25 summary page, "FlashAttention-3"
+ * paragraph and Fig 7; "PipeThreader and TileLang" page, section 4.1): for
+ * every batch b and head h, with inputs Q, K, V,
+ *     S = scale * Q K^T            (optionally causally masked)
+ *     P = softmax(S) row by row,   O = P V,
+ * computed in one fused kernel that streams K/V blocks (load_k, load_v),
+ * multiplies (mma_qk, mma_pv) and keeps an online softmax with output
+ * rescaling, so the N x N matrix never exists. The kernel also returns the
+ * per-row log-sum-exp of the scaled logits.
+ *
+ * Readings where the pages are silent (stated once, used by every entry):
+ *   - scale multiplies q.k before the softmax; callers usually pass
+ *     1/sqrt(d) rounded to float32;
+ *   - causal != 0: key j is visible to query i iff j <= i (square,
+ *     top-left aligned, diagonal included); masked pairs get zero weight;
+ *   - lse[i] = ln sum_{j visible} exp(scale * q_i . k_j)   (natural log).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Every entry point validates its arguments before any HIP
+ * call; on a nonzero return nothing was launched and no output was written. */
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = 1,   /* q, k, v, out or lse is NULL while B*H*N > 0        */
+  ATTN_ERR_BAD_SHAPE = 2,  /* B, H or N negative, or an element count overflows  */
+  ATTN_ERR_HEAD_DIM = 3,   /* d is not 64, 128 or 256                             */
+  ATTN_ERR_BAD_SCALE = 4,  /* scale is NaN, infinite or zero                      */
+  ATTN_ERR_MISALIGNED = 5, /* a pointer is not 16-byte aligned                    */
+  ATTN_ERR_HIP = 6,        /* the HIP runtime reported an error at launch         */
+  ATTN_ERR_BAD_VARIANT = 7 /* attn_fwd_variant: id out of range or unsuited to d */
+};
+
+/*
+ * attn_fwd -- fused attention forward on one GPU.
+ *
+ *   q, k, v : device pointers, bf16, dense row-major [B][H][N][d]
+ *   out     : device pointer, float32, [B][H][N][d]; fully overwritten
+ *   lse     : device pointer, float32, [B][H][N];   fully overwritten
+ *   B, H, N : batch, heads, sequence length (N >= 1 any value; tails masked)
+ *   d       : head dimension, one of 64, 128, 256
+ *   causal  : 0 = every key visible, nonzero = key j visible to query i iff j <= i
+ *   scale   : finite, nonzero float32 multiplier of q.k
+ *   stream  : hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * Ownership: the caller owns all five buffers; the library never allocates,
+ * frees, copies or synchronises. The call is asynchronous: it enqueues the
+ * kernel on `stream` and returns; device-side faults surface at the caller's
+ * next synchronisation. B*H*N == 0 returns ATTN_OK and launches nothing.
+ * Preconditions not checked: out and lse do not alias q, k, v or each other;
+ * each buffer holds the stated number of elements.
+ * Thread-safe and stateless: calls on different streams may run concurrently.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
+             int N, int d, int causal, float scale, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* attn_strerror(int status);
+
+/*
+ * Kernel variants, for the tile/depth sweep (PipeThreader summary page,
+ * "Profiler" paragraph and Fig 9: candidate schedules are filtered by an
+ * on-chip memory check and the final one is chosen by measured whole-program
+ * latency; "PipeThreader and TileLang" page, section 7: the autotuner runs a
+ * correctness check before it profiles).
+ *
+ * attn_num_variants : number of compiled variants.
+ * attn_variant_name : short description "d128_bm256_bn64_w8_..."; NULL if id
+ *                     is out of range.
+ * attn_variant_info : fills head_dim, block_m (query rows per workgroup),
+ *                     block_n (keys per pipeline stage), waves per workgroup,
+ *                     and lds_bytes; returns ATTN_ERR_BAD_VARIANT for a bad id.
+ * attn_fwd_variant  : attn_fwd forced onto variant `id`; same arguments,
+ *                     validation and semantics, plus ATTN_ERR_BAD_VARIANT when
+ *                     the variant does not serve head dimension d.
+ * attn_default_variant : the variant attn_fwd picks for (d, causal), or -1.
+ */
+int attn_num_variants(void);
+const char* attn_variant_name(int id);
+int attn_variant_info(int id, int* head_dim, int* block_m, int* block_n, int* waves,
+                      int* lds_bytes);
+int attn_default_variant(int d, int causal);
+int attn_fwd_variant(int id, const void* q, const void* k, const void* v, float* out, float* lse,
+                     int B, int H, int N, int d, int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,150 @@
+"""Thin Python binding of ``libattn.so`` (C ABI declared in include/attn.h).
+
+Argument marshalling only: every step of attention forward runs in the HIP
+kernels. The low-level functions take raw device pointers and sizes with the
+same names and argument order as the C entry points; ``attn_forward`` is a
+convenience wrapper that allocates ``out``/``lse`` with torch (device memory
+and streams are all torch is used for) and calls ``attn_fwd``.
+
+There is no fallback: if the compiled library is missing or fails to load,
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL_PTR = 1
+ATTN_ERR_BAD_SHAPE = 2
+ATTN_ERR_HEAD_DIM = 3
+ATTN_ERR_BAD_SCALE = 4
+ATTN_ERR_MISALIGNED = 5
+ATTN_ERR_HIP = 6
+ATTN_ERR_BAD_VARIANT = 7
+
+_lib = None
+
+_FWD_ARGS = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+             ctypes.c_void_p]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"attn status {status}: {attn_strerror(status)}")
+
+
+def load_library():
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it first (python -m software_pipelined_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = _FWD_ARGS
+    lib.attn_fwd_variant.restype = ctypes.c_int
+    lib.attn_fwd_variant.argtypes = [ctypes.c_int] + _FWD_ARGS
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_num_variants.restype = ctypes.c_int
+    lib.attn_num_variants.argtypes = []
+    lib.attn_variant_name.restype = ctypes.c_char_p
+    lib.attn_variant_name.argtypes = [ctypes.c_int]
+    lib.attn_variant_info.restype = ctypes.c_int
+    lib.attn_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int)] * 5
+    lib.attn_default_variant.restype = ctypes.c_int
+    lib.attn_default_variant.argtypes = [ctypes.c_int, ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------ C entry points
+
+def attn_fwd(q, k, v, out, lse, B, H, N, d, causal, scale, stream) -> int:
+    """Same arguments as the C ``attn_fwd``: device pointers (ints), sizes, stream handle."""
+    return load_library().attn_fwd(q, k, v, out, lse, B, H, N, d, int(causal), float(scale), stream)
+
+
+def attn_fwd_variant(id, q, k, v, out, lse, B, H, N, d, causal, scale, stream) -> int:
+    return load_library().attn_fwd_variant(id, q, k, v, out, lse, B, H, N, d, int(causal),
+                                           float(scale), stream)
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(status).decode()
+
+
+def attn_num_variants() -> int:
+    return load_library().attn_num_variants()
+
+
+def attn_variant_name(id: int):
+    r = load_library().attn_variant_name(id)
+    return None if r is None else r.decode()
+
+
+def attn_variant_info(id: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(5)]
+    st = load_library().attn_variant_info(id, *[ctypes.byref(x) for x in vals])
+    if st != ATTN_OK:
+        raise AttnError(st)
+    keys = ("head_dim", "block_m", "block_n", "waves", "lds_bytes")
+    return dict(zip(keys, (x.value for x in vals)))
+
+
+def attn_default_variant(d: int, causal: bool) -> int:
+    return load_library().attn_default_variant(d, int(causal))
+
+
+# ------------------------------------------------------------ torch convenience
+
+def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, variant=None,
+                 stream=None):
+    """Attention forward on torch tensors already on the GPU.
+
+    q, k, v: bfloat16 [B, H, N, d], contiguous, on a HIP device. Returns
+    (out float32 [B, H, N, d], lse float32 [B, H, N]). ``scale`` defaults to
+    float32(1/sqrt(d)). The kernel is enqueued on ``stream`` (default: torch's
+    current stream) and the call returns without synchronising.
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be on the GPU")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise TypeError("out and lse must be float32")
+    if tuple(out.shape) != (B, H, N, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out/lse shape mismatch")
+    if not (out.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("out and lse must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, N, d, causal, scale, handle)
+    st = attn_fwd(*args) if variant is None else attn_fwd_variant(variant, *args)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse

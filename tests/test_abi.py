@@ -1,0 +1,123 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every entry
+point declared in include/attn.h, and rejects bad arguments before any HIP
+call (so no GPU is needed). Also checks the build and bench host logic."""
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from software_pipelined_amd import attn as a, build
+    if not os.path.exists(a.LIB_PATH):
+        build.build_library()
+    a.load_library()
+    return a
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_strerror", "attn_num_variants", "attn_variant_name",
+              "attn_variant_info", "attn_default_variant", "attn_fwd_variant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(attn):
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20  # a fake 16-byte-aligned address; never dereferenced on these paths
+    good = (P, P, P, P, P)
+    assert attn.attn_fwd(0, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_NULL_PTR
+    assert attn.attn_fwd(*good, -1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_fwd(*good, 1, -2, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_fwd(*good, 1, 1, -16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
+    for d in (0, 32, 96, 192, 512):
+        assert attn.attn_fwd(*good, 1, 1, 16, d, 0, 0.1, None) == attn.ATTN_ERR_HEAD_DIM
+    for s in (float("nan"), float("inf"), float("-inf"), 0.0):
+        assert attn.attn_fwd(*good, 1, 1, 16, 128, 0, s, None) == attn.ATTN_ERR_BAD_SCALE
+    assert attn.attn_fwd(P + 2, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_MISALIGNED
+    assert attn.attn_fwd(P, P, P, P + 8, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_MISALIGNED
+    # empty problems are a no-op success, even with null pointers
+    assert attn.attn_fwd(0, 0, 0, 0, 0, 0, 4, 16, 128, 1, 0.1, None) == attn.ATTN_OK
+    assert attn.attn_fwd(0, 0, 0, 0, 0, 2, 4, 0, 64, 0, 0.1, None) == attn.ATTN_OK
+    # size overflow is a shape error
+    big = 1 << 30
+    assert attn.attn_fwd(*good, big, big, big, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
+
+
+def test_variant_table(attn):
+    n = attn.attn_num_variants()
+    assert n >= 3
+    seen_d = set()
+    for i in range(n):
+        info = attn.attn_variant_info(i)
+        name = attn.attn_variant_name(i)
+        assert name and f"d{info['head_dim']}" in name
+        assert info["block_m"] == 32 * info["waves"]
+        assert info["lds_bytes"] <= 160 * 1024
+        seen_d.add(info["head_dim"])
+    assert seen_d == {64, 128, 256}
+    assert attn.attn_variant_name(n) is None and attn.attn_variant_name(-1) is None
+    with pytest.raises(attn.AttnError):
+        attn.attn_variant_info(n)
+    for d in (64, 128, 256):
+        for c in (0, 1):
+            vid = attn.attn_default_variant(d, c)
+            assert 0 <= vid < n and attn.attn_variant_info(vid)["head_dim"] == d
+    assert attn.attn_default_variant(96, 0) == -1
+    P = 1 << 20
+    assert attn.attn_fwd_variant(n, P, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_VARIANT
+    d128 = attn.attn_default_variant(128, 0)
+    assert attn.attn_fwd_variant(d128, P, P, P, P, P, 1, 1, 16, 64, 0, 0.1, None) == attn.ATTN_ERR_BAD_VARIANT
+
+
+def test_strerror_covers_every_status(attn):
+    for st in range(8):
+        assert attn.attn_strerror(st) and attn.attn_strerror(st) != "unknown status"
+    assert attn.attn_strerror(99) == "unknown status"
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    import software_pipelined_amd.attn as a
+    monkeypatch.setattr(a, "_lib", None)
+    monkeypatch.setattr(a, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(FileNotFoundError):
+        a.attn_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 0, 1.0, None)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_product_path_never_imports_the_oracle():
+    """The HIP binding, build step and kernel sources never import, load or
+    link anything under oracle/."""
+    pkg = os.path.join(ROOT, "software_pipelined_amd")
+    pat = re.compile(r"^\s*(from|import)\s+oracle|attn_oracle|liboracle|oracle/", re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f"{f} references the oracle"
