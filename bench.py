@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--variant", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, run a plain device-to-device copy of this many "
+                         "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -108,6 +111,17 @@ def main():
     import torch
 
     from software_pipelined_amd import attn, build as hip_build, inputs
+
+    if args.copy_mib:
+        assert torch.cuda.is_available(), "bench needs a HIP device"
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_step": n * 4, "steps": args.warmup + args.steps}), flush=True)
+        return
 
     if not os.path.exists(attn.LIB_PATH):
         hip_build.build_library()

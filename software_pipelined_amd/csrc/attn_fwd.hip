@@ -10,23 +10,24 @@
 // the row log-sum-exp.
 //
 // gfx950 mapping (not the pages' H100 design; their TMA producer warps and
-// wgmma ping-pong are prior art):
-//   * one workgroup = NW wavefronts x 32 query rows (BM = 32*NW), one SIMD
-//     pair per two waves; each wave owns its 32 queries end to end;
+// wgmma warp groups are prior art):
+//   * a workgroup has NW wavefronts; each wave owns QT tiles of 32 query
+//     rows end to end (BM = 32*QT*NW rows per workgroup);
 //   * S is formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     K (from LDS) is the A operand and Q^T (kept in VGPRs for the whole
-//     loop) is the B operand, so each lane's accumulator column is one query
-//     and row max / row sum reduce within the lane plus one lane^32 swap
-//     (v_permlane32_swap);
+//     K (from LDS) is the A operand and Q^T (kept in registers for the whole
+//     loop) the B operand, so each lane's accumulator column is one query and
+//     row max / row sum reduce within the lane plus one lane^32 swap
+//     (v_permlane32_swap); with QT = 2 every K fragment read from LDS feeds
+//     two MFMAs;
 //   * O^T += V^T P^T with the same instruction: P^T goes straight from the
 //     S accumulators into the B operand (cvt to bf16, no LDS round trip),
 //     V^T is read with the gfx950 transposing LDS read ds_read_b64_tr_b16;
-//   * K/V blocks are double-buffered in LDS and filled with
-//     global_load_lds_dwordx4 (HBM -> LDS without VGPRs), one block ahead of
-//     the block being computed; the destination layout is XOR-swizzled per
-//     row by choosing which global chunk each lane fetches;
+//   * K/V blocks stream through an LDS ring filled with
+//     global_load_lds_dwordx4 (HBM -> LDS without VGPRs); the destination
+//     layout is XOR-swizzled per row by choosing which global chunk each lane
+//     fetches, so MFMA fragment reads are bank-conflict free;
 //   * exp2 runs on v_exp_f32 with scale*log2(e) folded into one FMA;
-//   * the O *= alpha rescale is skipped by a whole wave when none of its 32
+//   * the O *= alpha rescale is skipped by a whole wave when none of its
 //     rows raised its running max in the block (alpha == 1 exactly). The max
 //     itself is tracked exactly, never lazily: a stale max makes the
 //     dominant key's weight 2^delta instead of exactly 1, and its bf16
@@ -34,11 +35,16 @@
 //   * workgroup ids are remapped so that consecutive query tiles of one head
 //     run on one XCD (shared L2 for that head's K/V); causal grids start with
 //     the heaviest tiles.
+// Three schedules share the per-block step helpers (same arithmetic, bit for
+// bit): "simple" (steps in program order), "pingpong" (two wave groups take
+// turns on the matrix core) and "pipe" (each wave overlaps the softmax of
+// block j with the QK^T MFMAs of block j+1).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
 #include <limits.h>
+#include <string.h>
 
 #include "attn.h"
 
@@ -57,17 +63,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, int NW, int BN>
+// NW waves, QT query tiles of 32 per wave, BN keys per block, ST ring slots.
+template <int D, int NW, int BN, int QT = 1, int ST = 2>
 struct Tile {
-  static constexpr int BM = 32 * NW;                 // query rows per workgroup
+  static constexpr int BM = 32 * QT * NW;            // query rows per workgroup
   static constexpr int RC = D / 8;                   // 16-byte chunks per K/V row
   static constexpr int MAT_BYTES = BN * D * 2;       // one K (or V) block in LDS
   static constexpr int STAGE_BYTES = 2 * MAT_BYTES;  // K + V
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // two stages
-  static constexpr int LOADS = MAT_BYTES / (16 * 64 * NW);  // 1 KiB wave loads per matrix
+  static constexpr int LDS_BYTES = ST * STAGE_BYTES; // ring of ST stages
+  static constexpr int LOADS = MAT_BYTES / (16 * 64 * NW);  // 1 KiB wave copies per matrix
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
   static_assert(BN % 32 == 0, "BN multiple of 32");
   static_assert(LOADS * 16 * 64 * NW == MAT_BYTES, "block must split evenly over waves");
+  static_assert(ST >= 2, "at least double buffering");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
@@ -87,22 +95,43 @@ __device__ __forceinline__ int swz_v(int row) {
 
 // Issue the HBM -> LDS copy of BN rows (starting at row0) of one [N][D]
 // matrix. Every wave moves LOADS x 1 KiB; lane l's 16 bytes land at
-// dst + 16*l, so the swizzle is applied by choosing the source chunk.
-// Rows past N are clamped to row N-1 (finite data; those keys are masked).
+// dst + 16*l, so the swizzle is applied by choosing the source chunk. Full
+// blocks use a uniform block base plus a 32-bit per-lane offset (one VGPR per
+// copy); in the ragged last block rows past N are clamped to row N-1 (finite
+// data; those keys are masked).
+template <int D, int NW, int BN, bool IS_V>
+__device__ __forceinline__ uint32_t block_lane_offset(int t, int wave, int lane, int& row) {
+  using T = Tile<D, NW, BN>;
+  const int p = (t * NW + wave) * 64 + lane;
+  row = p / T::RC;
+  const int pc = p % T::RC;
+  const int c = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+  return (uint32_t)(row * (D * 2) + c * 16);
+}
+
 template <int D, int NW, int BN, bool IS_V>
 __device__ __forceinline__ void issue_block_load(const uint16_t* __restrict__ src, int row0, int N,
                                                  char* dst, int wave, int lane) {
   using T = Tile<D, NW, BN>;
+  const char* base = (const char*)src + (size_t)row0 * (D * 2);
+  if (row0 + BN <= N) {
 #pragma unroll
-  for (int t = 0; t < T::LOADS; ++t) {
-    const int slot0 = (t * NW + wave) * 64;
-    const int p = slot0 + lane;
-    const int row = p / T::RC;
-    const int pc = p % T::RC;
-    const int c = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
-    const int grow = min(row0 + row, N - 1);
-    const uint16_t* g = src + (size_t)grow * D + c * 8;
-    __builtin_amdgcn_global_load_lds((GLB_AS void*)g, (LDS_AS void*)(dst + slot0 * 16), 16, 0, 0);
+    for (int t = 0; t < T::LOADS; ++t) {
+      int row;
+      const uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
+      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + off),
+                                       (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < T::LOADS; ++t) {
+      int row;
+      uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
+      const int over = row0 + row - (N - 1);
+      if (over > 0) off -= (uint32_t)(over * (D * 2));  // clamp to row N-1
+      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + off),
+                                       (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
+    }
   }
 }
 
@@ -123,179 +152,603 @@ __device__ __forceinline__ int xcd_remap(int i, int G) {
   return x * q + min(x, r) + k;
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
-    int n_qtiles, float c_log2, int negate_q) {
-  using T = Tile<D, NW, BN>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+// ---------------------------------------------------------------- per-block steps
+// Each helper is one step of the per-block schedule; all kernels call the
+// same helpers in the same per-block order, so their results agree bit for
+// bit and differ only in how steps overlap.
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5;  // which half of the wave
-  const int lq = lane & 31;  // query column owned by this lane
-
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_qtiles;
-  const int tq = L % n_qtiles;
-  const int tile = CAUSAL ? (n_qtiles - 1 - tq) : tq;
-  const int q0 = tile * T::BM;
-  const int q0w = q0 + wave * 32;
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
-
-  // KV range of the workgroup and of this wave.
-  const int kv_end_wg = CAUSAL ? min(N, q0 + T::BM) : N;
-  const int kv_end_w = CAUSAL ? min(N, q0w + 32) : N;
-  const int nblk = (kv_end_wg + BN - 1) / BN;
-
-  // Prefetch block 0 before touching Q so the copies overlap the Q load.
-  issue_block_load<D, NW, BN, false>(Kh, 0, N, smem, wave, lane);
-  issue_block_load<D, NW, BN, true>(Vh, 0, N, smem + T::MAT_BYTES, wave, lane);
-
-  // Q^T as MFMA B operand: lane holds Q[q][kk*16 + h*8 .. +7] for its query q.
-  bf16x8 qf[D / 16];
-  {
-    const int qrow = min(q0w + lq, N - 1);
-    const uint16_t* qp = Qh + (size_t)qrow * D + h * 8;
+// Per-lane LDS byte offsets of the MFMA operand fragments within one K (or
+// V) block image. They depend only on the lane, so they are computed once;
+// the key-tile, half and ring-slot offsets are compile-time immediates.
+template <int D>
+struct LdsOffsets {
+  int k[D / 16];  // K fragment for d-chunk kk: row lq, 16-byte chunk 2kk+h
+  int v[D / 32];  // V^T transposed read for dim tile t (first of the 8-row pair)
+  __device__ __forceinline__ explicit LdsOffsets(int lane) {
+    const int h = lane >> 5, lq = lane & 31, ci = lane & 15, g2 = (lane >> 4) & 1;
+    const int swk = swz_k<D>(lq);  // equal for rows lq + 32*kb
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 raw = *(const u32x4*)(qp + kk * 16);
-      if (negate_q) raw ^= 0x80008000u;  // exact sign flip of 8 bf16 values
-      qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = lq * (D * 2) + (((2 * kk + h) ^ swk) << 4);
+    const int r0 = 4 * h + (ci >> 2);  // + 32*kb + 16*hf + 8*pair: swizzle-neutral offsets
+    const int swv = swz_v<D>(r0);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int dd = t * 32 + g2 * 16 + 4 * (ci & 3);
+      v[t] = r0 * (D * 2) + (((dd >> 3) ^ swv) << 4) + (dd & 7) * 2;
     }
   }
+};
 
-  f32x16 o[D / 32];
+// Scheduling patterns (sched_group_barrier masks: 0x008 MFMA, 0x100 DS
+// read, 0x002 VALU). Reads run PF reads ahead of the MFMAs that consume them;
+// each read feeds MR MFMAs.
+template <int NR, int RD, int MR, int PF>
+__device__ __forceinline__ void sched_mfma_with_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) o[t] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled logits, log2 units
-  float l_run = 0.f;        // this lane's half of the running row sum
-
-  const int qi = q0w + lq;  // this lane's query index (may be >= N in a ragged tile)
-
-  for (int j = 0; j < nblk; ++j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < nblk) {
-      char* st = smem + ((j + 1) & 1) * T::STAGE_BYTES;
-      issue_block_load<D, NW, BN, false>(Kh, (j + 1) * BN, N, st, wave, lane);
-      issue_block_load<D, NW, BN, true>(Vh, (j + 1) * BN, N, st + T::MAT_BYTES, wave, lane);
+  for (int i = 0; i < NR - PF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
+}
+template <int NR, int RD, int MR, int PF, int NV>
+__device__ __forceinline__ void sched_mfma_with_reads_and_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
+#pragma unroll
+  for (int i = 0; i < NR - PF; ++i) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
     }
-    const int kv0 = j * BN;
-    if (kv0 >= kv_end_w) continue;  // wave-uniform: block entirely masked for this wave
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PF * MR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
 
-    const char* Ks = smem + (j & 1) * T::STAGE_BYTES;
-    const char* Vs = Ks + T::MAT_BYTES;
+constexpr int kPfQK = 4;  // K fragments in flight ahead of mma_qk
+constexpr int kPfPV = 2;  // V fragment pairs in flight ahead of mma_pv
 
-    // ---- mma_qk: S^T[key][query] for BN keys, 32 keys per accumulator tile
-    f32x16 s[BN / 32];
+// mma_qk: S^T[key][query] for BN keys (K block image at Ks) against the
+// wave's QT query tiles. A operand = K rows (ds_read_b128), B operand = Q^T.
+// All fragment reads are issued up front in program order; the caller's
+// scheduling pattern places them ahead of their MFMAs.
+template <int D, int BN, int QT>
+__device__ __forceinline__ void qk_block(const char* Ks, const LdsOffsets<D>& off,
+                                         const bf16x8 (&qf)[QT][D / 16],
+                                         f32x16 (&s)[QT][BN / 32]) {
+  constexpr int NKB = BN / 32;
+  bf16x8 kf[D / 16][NKB];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + lq;
-      const char* rbase = Ks + row * (D * 2);
-      const int sw = swz_k<D>(row);
+  for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int ch = (2 * kk + h) ^ sw;
-        bf16x8 a = *(LDS_AS const bf16x8*)(rbase + ch * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
-      }
-    }
+    for (int kb = 0; kb < NKB; ++kb)
+      kf[kk][kb] = *(LDS_AS const bf16x8*)(Ks + off.k[kk] + kb * 32 * (D * 2));
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[qt][kb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        s[qt][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[qt][kk], s[qt][kb], 0, 0, 0);
+}
 
-    // ---- mask (only blocks that straddle the diagonal or the end of K)
-    const bool need_mask = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0w);
-    if (need_mask) {
+// Masked pairs (key past N, or key after the query when causal) get -inf.
+// qi0 = this lane's query in tile 0; tile qt holds queries qi0 + 32*qt.
+template <int BN, int QT, bool CAUSAL>
+__device__ __forceinline__ void mask_block(f32x16 (&s)[QT][BN / 32], int kv0, int qi0, int N,
+                                           int lane) {
+  const int h = lane >> 5;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool dead = (key >= N) || (CAUSAL && key > qi);
-          s[kb][r] = dead ? -INFINITY : s[kb][r];
-        }
-    }
-
-    // ---- online softmax
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) bmax = fmaxf(bmax, fmaxf(s[kb][r], s[kb][r + 1]));
-    bmax = swap32_max(bmax);
-    const float mb = bmax * c_log2;
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if unchanged, 0 at start
-    m_run = m_new;
-
-    float psum = 0.f;
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_new));
-        s[kb][r] = p;
-        psum += p;
+        const int key = kv0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        const bool dead = (key >= N) || (CAUSAL && key > qi0 + 32 * qt);
+        s[qt][kb][r] = dead ? -INFINITY : s[qt][kb][r];
       }
-    l_run = __builtin_fmaf(l_run, alpha, psum);
+}
 
-    // ---- rescale (skipped by the whole wave when no row moved its max)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+// softmax (per query tile): new running max, alpha = exp2(m_old - m_new),
+// p = exp2(c*s - m) with the row sum taken from fp32 p, and P^T packed to
+// bf16 (RNE) as the B operand of mma_pv: pb[qt][2*kb + hf] holds accumulator
+// registers 8*hf..8*hf+7 of key tile kb. alpha is 1 exactly when a row's max
+// did not move.
+template <int BN, int QT>
+__device__ __forceinline__ void softmax_block(const f32x16 (&s)[QT][BN / 32],
+                                              bf16x8 (&pb)[QT][BN / 16], float c_log2,
+                                              float (&m_run)[QT], float (&l_run)[QT],
+                                              float (&alpha)[QT]) {
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) o[t] *= alpha;
-    }
-
-    // ---- mma_pv: O^T[dim][query] += V^T[dim][key] P^T[key][query]
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int c = (r >> 2) & 3;
+        mx[c] = fmaxf(mx[c], fmaxf(s[qt][kb][r], s[qt][kb][r + 1]));
+        mx[c] = fmaxf(mx[c], fmaxf(s[qt][kb][r + 2], s[qt][kb][r + 3]));
+      }
+    float bmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    bmax = swap32_max(bmax);
+    const float m_new = fmaxf(m_run[qt], bmax * c_log2);
+    alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 on the first block
+    m_run[qt] = m_new;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        // B operand: 8 keys of this lane's half, taken from accumulator
-        // registers 8*hf .. 8*hf+7 (keys kb*32 + 16*hf + {0..3, 8..11} + 4*h).
         f32x8 pv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[kb][8 * hf + e];
-        const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-        // A operand rows: the same 8 keys, read transposed from V.
-        const int kbase0 = kb * 32 + 16 * hf + 4 * h;
-        const int ci = lane & 15;
-        const int g2 = (lane >> 4) & 1;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const int dd = t * 32 + g2 * 16 + 4 * (ci & 3);
-          const int chunk = dd >> 3;
-          const int within = (dd & 7) * 2;
-          const int r0 = kbase0 + (ci >> 2);
-          const int r1 = r0 + 8;
-          const char* a0 = Vs + r0 * (D * 2) + ((chunk ^ swz_v<D>(r0)) * 16) + within;
-          const char* a1 = Vs + r1 * (D * 2) + ((chunk ^ swz_v<D>(r1)) * 16) + within;
-          i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
-          i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a1);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[t], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kb][8 * hf + e], c_log2, -m_new));
+          pv[e] = p;
+          ps[e & 3] += p;
         }
+        pb[qt][2 * kb + hf] = __builtin_convertvector(pv, bf16x8);
       }
-    }
+    l_run[qt] = __builtin_fmaf(l_run[qt], alpha[qt], (ps[0] + ps[1]) + (ps[2] + ps[3]));
   }
+}
 
-  // ---- epilogue: normalise, write O and LSE
-  const float l_tot = swap32_sum(l_run);
-  const float inv = 1.0f / l_tot;
-  if (qi < N) {
-    float* orow = O + head + (size_t)qi * D;
+// rescale: O *= alpha, skipped by the whole wave when no row moved its max.
+template <int D, int QT>
+__device__ __forceinline__ void rescale_block(f32x16 (&o)[QT][D / 32], const float (&alpha)[QT]) {
+  bool moved = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) moved = moved || (alpha[qt] != 1.0f);
+  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) o[qt][t] *= alpha[qt];
+  }
+}
+
+// mma_pv: O^T[dim][query] += V^T[dim][key] P^T[key][query]. The A operand
+// holds, for dim row t*32 + (lane & 31), the same 8 keys as this lane's half
+// of the B operand (keys kb*32 + 16*hf + 4*h + {0..3, 8..11}), read as two
+// 4-key transposed loads (ds_read_b64_tr_b16) 8 rows apart; each V fragment
+// feeds QT MFMAs.
+template <int D, int BN, int QT>
+__device__ __forceinline__ void pv_block(const char* Vs, const LdsOffsets<D>& off,
+                                         const bf16x8 (&pb)[QT][BN / 16],
+                                         f32x16 (&o)[QT][D / 32]) {
+  constexpr int NP = BN / 16;
+  i16x4 va[NP][D / 32][2];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)  // p = 2*kb + hf: rows p*16 + ...
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 w = {o[t][4 * g] * inv, o[t][4 * g + 1] * inv, o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv};
-        *(f32x4*)(orow + t * 32 + g * 8 + h * 4) = w;
-      }
-    if (h == 0) LSE[(size_t)bh * N + qi] = kLn2 * (m_run + __builtin_amdgcn_logf(l_tot));
+      for (int r = 0; r < 2; ++r)
+        va[p][t][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(Vs + off.v[t] + (p * 16 + r * 8) * (D * 2)));
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[p][t][0], va[p][t][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        o[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt][p], o[qt][t], 0, 0, 0);
+    }
+}
+
+// Load the wave's Q^T fragments (B operand of mma_qk): lane holds
+// Q[q][kk*16 + h*8 .. +7] for its query q of each tile (rows past N clamped).
+template <int D, int QT>
+__device__ __forceinline__ void load_q(const uint16_t* Qh, int q0w, int N, int negate_q,
+                                       bf16x8 (&qf)[QT][D / 16], int lane) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qrow = min(q0w + 32 * qt + (lane & 31), N - 1);
+    const uint16_t* qp = Qh + (size_t)qrow * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 raw = *(const u32x4*)(qp + kk * 16);
+      if (negate_q) raw ^= 0x80008000u;  // exact sign flip of 8 bf16 values
+      qf[qt][kk] = __builtin_bit_cast(bf16x8, raw);
+    }
   }
+}
+
+// Epilogue: O = O_acc / l and LSE = ln2 * (m + log2 l), stored for rows < N.
+template <int D, int QT>
+__device__ __forceinline__ void store_rows(float* O, float* LSE, size_t head, size_t bh, int N,
+                                           int qi0, const f32x16 (&o)[QT][D / 32],
+                                           const float (&m_run)[QT], const float (&l_run)[QT],
+                                           int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qi = qi0 + 32 * qt;
+    const float l_tot = swap32_sum(l_run[qt]);
+    const float inv = 1.0f / l_tot;
+    if (qi < N) {
+      float* orow = O + head + (size_t)qi * D;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w = {o[qt][t][4 * g] * inv, o[qt][t][4 * g + 1] * inv, o[qt][t][4 * g + 2] * inv,
+                     o[qt][t][4 * g + 3] * inv};
+          *(f32x4*)(orow + t * 32 + g * 8 + h * 4) = w;
+        }
+      if (h == 0) LSE[bh * N + qi] = kLn2 * (m_run[qt] + __builtin_amdgcn_logf(l_tot));
+    }
+  }
+}
+
+// Everything a block step needs besides the per-block registers.
+struct Ctx {
+  const uint16_t* Kh;
+  const uint16_t* Vh;
+  size_t head;
+  int bh;
+  int N, nblk, kv_end_w, q0w, qi0, wave, lane;
+  float c_log2;
+};
+
+// Workgroup -> (batch*head, query tile) and the per-wave key range.
+template <int D, int BM, int BN, int WROWS, bool CAUSAL>
+__device__ __forceinline__ Ctx make_ctx(const uint16_t* K, const uint16_t* V, int N, int n_qtiles,
+                                        float c_log2) {
+  Ctx c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  c.bh = L / n_qtiles;
+  const int tq = L % n_qtiles;
+  const int tile = CAUSAL ? (n_qtiles - 1 - tq) : tq;
+  const int q0 = tile * BM;
+  c.q0w = q0 + c.wave * WROWS;
+  c.qi0 = c.q0w + (c.lane & 31);
+  c.head = (size_t)c.bh * N * D;
+  c.Kh = K + c.head;
+  c.Vh = V + c.head;
+  c.N = N;
+  const int kv_end_wg = CAUSAL ? min(N, q0 + BM) : N;
+  c.kv_end_w = CAUSAL ? min(N, c.q0w + WROWS) : N;
+  c.nblk = (kv_end_wg + BN - 1) / BN;
+  c.c_log2 = c_log2;
+  return c;
+}
+
+// Does block j straddle the diagonal (first query of the wave) or the end of K?
+template <int BN, bool CAUSAL>
+__device__ __forceinline__ bool block_needs_mask(const Ctx& c, int kv0) {
+  return (kv0 + BN > c.N) || (CAUSAL && kv0 + BN - 1 > c.q0w);
+}
+
+// LDS images of an ST-slot ring: K slot s at s*MAT, V slot s at (ST+s)*MAT.
+template <int D, int BN, int ST>
+__device__ __forceinline__ char* k_slot(char* smem, int s) {
+  return smem + s * (BN * D * 2);
+}
+template <int D, int BN, int ST>
+__device__ __forceinline__ char* v_slot(char* smem, int s) {
+  return smem + (ST + s) * (BN * D * 2);
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// (copies complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------- simple kernel
+// Blocks stream through an ST-slot ring (block j in slot j mod ST): at the
+// top of block j every wave waits for its share of block j's copies, meets
+// the others at the barrier (so slot (j-1) mod ST is no longer read), and
+// starts the copies of block j+ST-1 into that slot; then the steps of block j
+// run in program order. The reference schedule the overlapped kernels are
+// checked against (bit for bit).
+template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int SLOT>
+__device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
+                                             const LdsOffsets<D>& off,
+                                             const bf16x8 (&qf)[QT][D / 16],
+                                             f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
+                                             float (&l_run)[QT]) {
+  constexpr int PER_BLOCK = 2 * Tile<D, NW, BN>::LOADS;  // copy instructions per block per wave
+  if (j + ST - 2 < c.nblk)
+    wait_vmcnt<(ST - 2) * PER_BLOCK>();  // blocks j+1 .. j+ST-2 may stay in flight
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+  if (j + ST - 1 < c.nblk) {
+    constexpr int NS = (SLOT + ST - 1) % ST;
+    issue_block_load<D, NW, BN, false>(c.Kh, (j + ST - 1) * BN, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane);
+    issue_block_load<D, NW, BN, true>(c.Vh, (j + ST - 1) * BN, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane);
+  }
+  const int kv0 = j * BN;
+  if (kv0 >= c.kv_end_w) return;  // wave-uniform: the whole block is masked for this wave
+  f32x16 s[QT][BN / 32];
+  qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, SLOT), off, qf, s);
+  sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+  if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
+  bf16x8 pb[QT][BN / 16];
+  float alpha[QT];
+  softmax_block<BN, QT>(s, pb, c.c_log2, m_run, l_run, alpha);
+  rescale_block<D, QT>(o, alpha);
+  pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, SLOT), off, pb, o);
+  sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int ST>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_simple(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int negate_q) {
+  using T = Tile<D, NW, BN, QT, ST>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
+
+  // Q first, then blocks 0 .. ST-2 (so the in-loop waits count block copies only)
+  bf16x8 qf[QT][D / 16];
+  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
+#pragma unroll
+  for (int b = 0; b < ST - 1; ++b)
+    if (b < c.nblk) {
+      issue_block_load<D, NW, BN, false>(c.Kh, b * BN, N, k_slot<D, BN, ST>(smem, b), c.wave, c.lane);
+      issue_block_load<D, NW, BN, true>(c.Vh, b * BN, N, v_slot<D, BN, ST>(smem, b), c.wave, c.lane);
+    }
+  const LdsOffsets<D> off(c.lane);
+  f32x16 o[QT][D / 32];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
+  for (int j = 0; j < c.nblk; j += ST) {
+    simple_block<D, NW, BN, QT, CAUSAL, ST, 0>(c, smem, j, off, qf, o, m_run, l_run);
+    if (j + 1 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 1 % ST>(c, smem, j + 1, off, qf, o, m_run, l_run);
+    if (ST > 2 && j + 2 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 2 % ST>(c, smem, j + 2, off, qf, o, m_run, l_run);
+    if (ST > 3 && j + 3 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 3 % ST>(c, smem, j + 3, off, qf, o, m_run, l_run);
+  }
+  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
+}
+
+// ---------------------------------------------------------------- pipelined kernel
+// Software-pipelined schedule inside each wave (the pages' FlashAttention-
+// forward schedule found by Twill, section 3.1 of the software-pipelining
+// page: the first GEMM is hoisted into the loop prologue so exp latency is
+// never exposed, and one tile's exp overlaps another tile's GEMM; restated
+// for gfx950, where one wave interleaving its own MFMAs and VALU keeps both
+// units busy):
+//   prologue : K_0, V_0, K_1 -> LDS; S_0 = Q K_0^T
+//   block j  : copies of K_{j+2}, V_{j+1} in flight (one barrier per block)
+//              while the wave issues mma_qk(K_{j+1}) and, between those
+//              MFMAs, the softmax of S_j; then rescale and mma_pv(V_j).
+// K runs two blocks ahead of its use and V one; LDS holds two K and two V
+// slots. At the top of block j each wave waits for K_{j+1} and V_j; after the
+// barrier K_j (read by mma_qk in block j-1) and V_{j-1} (read by mma_pv in
+// block j-1) are free.
+template <int D, int NW, int BN, int QT, bool CAUSAL, int SLOT>
+__device__ __forceinline__ void pipe_block(const Ctx& c, char* smem, int j, const LdsOffsets<D>& off,
+                                           const bf16x8 (&qf)[QT][D / 16],
+                                           f32x16 (&s_cur)[QT][BN / 32],
+                                           f32x16 (&s_nxt)[QT][BN / 32], f32x16 (&o)[QT][D / 32],
+                                           float (&m_run)[QT], float (&l_run)[QT]) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (j + 2 < c.nblk)
+    issue_block_load<D, NW, BN, false>(c.Kh, (j + 2) * BN, c.N, k_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane);
+  if (j + 1 < c.nblk)
+    issue_block_load<D, NW, BN, true>(c.Vh, (j + 1) * BN, c.N, v_slot<D, BN, 2>(smem, SLOT ^ 1), c.wave, c.lane);
+  const int kv0 = j * BN;
+  if (kv0 >= c.kv_end_w) return;  // wave-uniform
+  const bool nxt = kv0 + BN < c.kv_end_w;
+  const bool msk = block_needs_mask<BN, CAUSAL>(c, kv0);
+  bf16x8 pb[QT][BN / 16];
+  float alpha[QT];
+  if (nxt && !msk) {
+    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+    softmax_block<BN, QT>(s_cur, pb, c.c_log2, m_run, l_run, alpha);
+    sched_mfma_with_reads_and_valu<(D / 16) * (BN / 32), 1, QT, kPfQK, 9>();
+  } else {
+    if (nxt) {
+      qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+      sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+    }
+    if (msk) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
+    softmax_block<BN, QT>(s_cur, pb, c.c_log2, m_run, l_run, alpha);
+  }
+  rescale_block<D, QT>(o, alpha);
+  pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT), off, pb, o);
+  sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int negate_q) {
+  using T = Tile<D, NW, BN, QT, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
+
+  // prologue: Q; K_0, V_0, K_1 in flight; S_0 = Q K_0^T
+  bf16x8 qf[QT][D / 16];
+  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
+  issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
+  issue_block_load<D, NW, BN, true>(c.Vh, 0, N, v_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
+  if (c.nblk > 1)
+    issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
+  const LdsOffsets<D> off(c.lane);
+  f32x16 o[QT][D / 32];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
+  f32x16 sa[QT][BN / 32], sb[QT][BN / 32];
+  wait_vmcnt<0>();
+  __syncthreads();
+  qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, sa);  // block 0 is never skipped
+  sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+
+  // two blocks per trip so S_cur / S_next swap roles without register copies
+  // and every LDS slot offset is an immediate
+  for (int j = 0; j < c.nblk; j += 2) {
+    pipe_block<D, NW, BN, QT, CAUSAL, 0>(c, smem, j, off, qf, sa, sb, o, m_run, l_run);
+    if (j + 1 < c.nblk) pipe_block<D, NW, BN, QT, CAUSAL, 1>(c, smem, j + 1, off, qf, sb, sa, o, m_run, l_run);
+  }
+  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
+}
+
+// ---------------------------------------------------------------- ping-pong kernel
+// Two wave groups per workgroup (A = waves 0..NW/2-1, B = the rest; each
+// SIMD holds one wave of each) alternate on the matrix core, half a block
+// apart -- the pages' forward schedule in which two compute groups take turns
+// on the matrix unit while the other runs the softmax (software-pipelining
+// page, section 3.1), restated for gfx950 with s_barrier as the turn signal.
+// Intervals t = 0, 1, ..., 2n (n = KV blocks) are separated by barriers:
+//
+//   interval   group A                   group B
+//   prologue   S_0 = Q K_0^T              -
+//   2j         softmax_j (+rescale)       mma_pv(V_{j-1}), S_j = Q K_j^T
+//   2j+1       mma_pv(V_j), S_{j+1}       softmax_j (+rescale)
+//
+// K_j is read in intervals 2j-1 (A) and 2j (B), V_j in 2j+1 (A) and 2j+2
+// (B); at barrier 2m+1 the copies of K_{m+2} (over K_m) and V_{m+1} (over
+// V_{m-1}) start, and each wave waits for them before barrier 2m+3. Each
+// group runs its own loop; both pass the same number of barriers.
+template <int D, int NW, int BN, int QT, bool CAUSAL, int VS, int KS>
+__device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int jp,
+                                                   const LdsOffsets<D>& off,
+                                                   const bf16x8 (&qf)[QT][D / 16],
+                                                   f32x16 (&s)[QT][BN / 32],
+                                                   const bf16x8 (&pb)[QT][BN / 16],
+                                                   f32x16 (&o)[QT][D / 32]) {
+  if (jp >= 0 && jp < c.nblk && jp * BN < c.kv_end_w) {
+    pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, VS), off, pb, o);
+    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
+  }
+  const int jq = jp + 1;
+  if (jq < c.nblk && jq * BN < c.kv_end_w) {
+    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, KS), off, qf, s);
+    sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+  }
+}
+
+template <int D, int BN, int QT, bool CAUSAL>
+__device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (&s)[QT][BN / 32],
+                                                   bf16x8 (&pb)[QT][BN / 16],
+                                                   f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
+                                                   float (&l_run)[QT]) {
+  if (j < c.nblk && j * BN < c.kv_end_w) {
+    const int kv0 = j * BN;
+    if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
+    float alpha[QT];
+    softmax_block<BN, QT>(s, pb, c.c_log2, m_run, l_run, alpha);
+    rescale_block<D, QT>(o, alpha);
+  }
+}
+
+// Start of an odd interval t = 2m+1: every wave waits for its share of the
+// copies started two intervals ago, meets the others at the barrier, then
+// starts K_{m+2} (over K_m, slot MS) and V_{m+1} (over V_{m-1}, slot MS^1).
+template <int D, int NW, int BN, int MS>
+__device__ __forceinline__ void pingpong_odd_barrier(const Ctx& c, char* smem, int m) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (m + 2 < c.nblk)
+    issue_block_load<D, NW, BN, false>(c.Kh, (m + 2) * BN, c.N, k_slot<D, BN, 2>(smem, MS), c.wave, c.lane);
+  if (m + 1 < c.nblk)
+    issue_block_load<D, NW, BN, true>(c.Vh, (m + 1) * BN, c.N, v_slot<D, BN, 2>(smem, MS ^ 1), c.wave, c.lane);
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_pingpong(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int negate_q) {
+  using T = Tile<D, NW, BN, QT, 2>;
+  static_assert(NW % 2 == 0, "two wave groups");
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
+
+  bf16x8 qf[QT][D / 16];
+  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
+  issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
+  issue_block_load<D, NW, BN, true>(c.Vh, 0, N, v_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
+  if (c.nblk > 1)
+    issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
+  const LdsOffsets<D> off(c.lane);
+  f32x16 o[QT][D / 32];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
+  f32x16 s[QT][BN / 32];
+  bf16x8 pb[QT][BN / 16];
+  wait_vmcnt<0>();
+  __syncthreads();
+  const int n = c.nblk;
+  // Both groups pass 2n+1 barriers after the prologue one.
+  if (c.wave < NW / 2) {
+    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, s);  // S_0 (block 0 is never skipped)
+    sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+    for (int j = 0; j < n; j += 2) {
+      // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
+      __syncthreads();
+      pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
+      pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o);
+      if (j + 1 < n) {  // block j+1 (odd): slots swap
+        __syncthreads();
+        pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
+        pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
+        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o);
+      }
+    }
+    __syncthreads();  // t = 2n: group B's last mma_pv
+  } else {
+    for (int j = 0; j < n; j += 2) {
+      // block j (even): [t=2j] pv(j-1) from V slot 1, qk(j) from K slot 0 | [t=2j+1] softmax
+      __syncthreads();
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o);
+      pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
+      pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
+      if (j + 1 < n) {
+        __syncthreads();
+        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o);
+        pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
+        pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
+      }
+    }
+    __syncthreads();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
+    if (n & 1)
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, n - 1, off, qf, s, pb, o);
+    else
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, n - 1, off, qf, s, pb, o);
+  }
+  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
 
 // ---------------------------------------------------------------- host side
@@ -303,22 +756,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 typedef hipError_t (*launch_fn)(const void*, const void*, const void*, float*, float*, int, int,
                                 int, int, float, hipStream_t);
 
-template <int D, int NW, int BN>
+enum Schedule { kSimple = 0, kPipelined = 1, kPingPong = 2 };
+
+template <int D, int NW, int BN, int QT, int SCHED, int ST>
 hipError_t launch(const void* q, const void* k, const void* v, float* out, float* lse, int B,
                   int H, int N, int causal, float scale, hipStream_t stream) {
-  using T = Tile<D, NW, BN>;
+  using T = Tile<D, NW, BN, QT, ST>;
   const int n_qt = (N + T::BM - 1) / T::BM;
   const long long G = (long long)B * H * n_qt;
   const float c = fabsf(scale) * kLog2e;
   const int neg = scale < 0.f;
-  if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BN, true>), dim3((unsigned)G), dim3(NW * 64), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, out,
-                       lse, N, n_qt, c, neg);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BN, false>), dim3((unsigned)G), dim3(NW * 64), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, out,
-                       lse, N, n_qt, c, neg);
+  const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
+  const dim3 grid((unsigned)G), block(NW * 64);
+  if constexpr (SCHED == kPingPong) {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+    else
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+  } else if constexpr (SCHED == kPipelined) {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+    else
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+    else
+      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, false, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+  }
   return hipGetLastError();
 }
 
@@ -328,16 +793,31 @@ struct Variant {
   launch_fn fn;
 };
 
-#define VARIANT(NAME, D, NW, BN) \
-  Variant { NAME, D, 32 * NW, BN, NW, Tile<D, NW, BN>::LDS_BYTES, &launch<D, NW, BN> }
+#define VARIANT(NAME, D, NW, BN, QT, SCHED, ST)                                        \
+  Variant {                                                                            \
+    NAME, D, 32 * QT * NW, BN, NW, Tile<D, NW, BN, QT, ST>::LDS_BYTES,                 \
+        &launch<D, NW, BN, QT, SCHED, ST>                                              \
+  }
 
+// Name fields: head dim, query rows per workgroup, keys per block, waves,
+// query tiles per wave, LDS ring slots, schedule.
 const Variant kVariants[] = {
-    VARIANT("d64_bm256_bn64_w8", 64, 8, 64),     // 0
-    VARIANT("d128_bm256_bn64_w8", 128, 8, 64),   // 1
-    VARIANT("d256_bm128_bn64_w4", 256, 4, 64),   // 2
-    VARIANT("d64_bm128_bn64_w4", 64, 4, 64),     // 3
-    VARIANT("d128_bm128_bn64_w4", 128, 4, 64),   // 4
-    VARIANT("d64_bm256_bn128_w8", 64, 8, 128),   // 5
+    VARIANT("d64_bm256_bn64_w8_q1_st2_simple", 64, 8, 64, 1, kSimple, 2),         // 0
+    VARIANT("d128_bm256_bn64_w8_q1_st2_simple", 128, 8, 64, 1, kSimple, 2),       // 1
+    VARIANT("d256_bm128_bn64_w4_q1_st2_simple", 256, 4, 64, 1, kSimple, 2),       // 2
+    VARIANT("d64_bm256_bn64_w4_q2_st2_pipe", 64, 4, 64, 2, kPipelined, 2),        // 3
+    VARIANT("d128_bm256_bn64_w4_q2_st2_pipe", 128, 4, 64, 2, kPipelined, 2),      // 4
+    VARIANT("d128_bm256_bn64_w8_q1_st2_pingpong", 128, 8, 64, 1, kPingPong, 2),   // 5
+    VARIANT("d64_bm256_bn64_w8_q1_st2_pingpong", 64, 8, 64, 1, kPingPong, 2),     // 6
+    VARIANT("d128_bm256_bn64_w4_q2_st2_simple", 128, 4, 64, 2, kSimple, 2),       // 7
+    VARIANT("d128_bm128_bn64_w4_q1_st2_pipe", 128, 4, 64, 1, kPipelined, 2),      // 8
+    VARIANT("d256_bm128_bn64_w4_q1_st2_pipe", 256, 4, 64, 1, kPipelined, 2),      // 9
+    VARIANT("d128_bm256_bn64_w8_q1_st4_simple", 128, 8, 64, 1, kSimple, 4),       // 10
+    VARIANT("d128_bm256_bn32_w8_q1_st2_simple", 128, 8, 32, 1, kSimple, 2),       // 11
+    VARIANT("d128_bm256_bn32_w4_q2_st2_pipe", 128, 4, 32, 2, kPipelined, 2),      // 12
+    VARIANT("d64_bm128_bn32_w4_q1_st2_simple", 64, 4, 32, 1, kSimple, 2),         // 13
+    VARIANT("d64_bm256_bn32_w4_q2_st2_pipe", 64, 4, 32, 2, kPipelined, 2),        // 14
+    VARIANT("d128_bm256_bn32_w4_q2_st2_simple", 128, 4, 32, 2, kSimple, 2),       // 15
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -355,7 +835,9 @@ int validate(const void* q, const void* k, const void* v, const float* out, cons
              int B, int H, int N, int d, float scale, int bm) {
   if (B < 0 || H < 0 || N < 0) return ATTN_ERR_BAD_SHAPE;
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEAD_DIM;
-  if (!isfinite(scale) || scale == 0.f) return ATTN_ERR_BAD_SCALE;
+  uint32_t sbits;
+  memcpy(&sbits, &scale, sizeof sbits);  // bit test: immune to fast-math folding
+  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
   long long bh = 0, rows = 0, elems = 0, grid = 0;
   if (__builtin_mul_overflow((long long)B, (long long)H, &bh) ||
       __builtin_mul_overflow(bh, (long long)N, &rows) ||

@@ -72,7 +72,7 @@ def test_variant_table(attn):
         info = attn.attn_variant_info(i)
         name = attn.attn_variant_name(i)
         assert name and f"d{info['head_dim']}" in name
-        assert info["block_m"] == 32 * info["waves"]
+        assert info["block_m"] % (32 * info["waves"]) == 0  # 32-row query tiles per wave
         assert info["lds_bytes"] <= 160 * 1024
         seen_d.add(info["head_dim"])
     assert seen_d == {64, 128, 256}

@@ -185,3 +185,36 @@ def test_device_pointer_errors():
     assert attn.attn_fwd_variant(0, p, p, p, o.data_ptr(), l.data_ptr(), 1, 1, 64, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_VARIANT
     # outputs untouched on error
     assert float(o.abs().sum()) == 0.0
+
+
+def test_overlapped_schedules_match_simple_schedule_bitwise():
+    """Every schedule (deeper rings, pipelined, ping-pong) runs the same
+    per-block arithmetic as the double-buffered simple kernel of the same
+    tiling, only overlapped; any LDS-ring or wait hazard shows up as a bit
+    difference."""
+    from software_pipelined_amd import attn
+    # reference per (head dim, keys per block): the double-buffered simple
+    # schedule; the per-row arithmetic depends only on those two
+    refs, pairs = {}, []
+    for i in range(attn.attn_num_variants()):
+        info = attn.attn_variant_info(i)
+        name = attn.attn_variant_name(i)
+        if name.endswith("_st2_simple"):
+            refs.setdefault((info["head_dim"], info["block_n"]), i)
+    for i in range(attn.attn_num_variants()):
+        info = attn.attn_variant_info(i)
+        ref = refs.get((info["head_dim"], info["block_n"]))
+        if ref is not None and ref != i:
+            pairs.append((i, ref))
+    assert pairs
+    for vid, ref in pairs:
+        d = attn.attn_variant_info(vid)["head_dim"]
+        for causal in (False, True):
+            for N in (1, 100, 1000):
+                _say(f"case differential {attn.attn_variant_name(vid)} vs {attn.attn_variant_name(ref)} "
+                     f"N{N} causal={causal}")
+                q, k, v = I.gen_qkv(2, 2, N, d, seed=N + d, key_stress=True)
+                o1, l1 = run_gpu(q, k, v, causal, I.default_scale(d), variant=vid)
+                o2, l2 = run_gpu(q, k, v, causal, I.default_scale(d), variant=ref)
+                np.testing.assert_array_equal(o1, o2)
+                np.testing.assert_array_equal(l1, l2)
