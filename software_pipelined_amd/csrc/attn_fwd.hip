@@ -135,6 +135,19 @@ __device__ __forceinline__ void issue_block_load(const uint16_t* __restrict__ sr
   }
 }
 
+// One copy instruction (t) of a block, branch-free: rows past N-1 are
+// clamped to N-1 per lane. Used where copies are interleaved with MFMAs.
+template <int D, int NW, int BN, bool IS_V>
+__device__ __forceinline__ void issue_copy(const uint16_t* __restrict__ src, int row0, int N, char* dst,
+                                           int wave, int lane, int t) {
+  int row;
+  const uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
+  const int over = max(row0 + row - (N - 1), 0);
+  const char* base = (const char*)src + (size_t)row0 * (D * 2);
+  __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + (off - (uint32_t)(over * (D * 2)))),
+                                   (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
+}
+
 __device__ __forceinline__ float swap32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -192,6 +205,24 @@ __device__ __forceinline__ void sched_mfma_with_reads() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
 }
+// As above, with NVM copy instructions (0x020 VMEM read) spread evenly over
+// the MFMA stream so the texture path never sees a burst.
+template <int I, int STEPS, int RD, int MR, int NVM>
+__device__ __forceinline__ void sched_copy_steps() {
+  if constexpr (I < STEPS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    constexpr int due = ((I + 1) * NVM) / STEPS - (I * NVM) / STEPS;
+    if constexpr (due > 0) __builtin_amdgcn_sched_group_barrier(0x010, due, 0);
+    sched_copy_steps<I + 1, STEPS, RD, MR, NVM>();
+  }
+}
+template <int NR, int RD, int MR, int PF, int NVM>
+__device__ __forceinline__ void sched_mfma_with_reads_and_copies() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
+  sched_copy_steps<0, NR - PF, RD, MR, NVM>();
+  __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
+}
 template <int NR, int RD, int MR, int PF, int NV>
 __device__ __forceinline__ void sched_mfma_with_reads_and_valu() {
   __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
@@ -229,6 +260,39 @@ __device__ __forceinline__ void qk_block(const char* Ks, const LdsOffsets<D>& of
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       kf[kk][kb] = *(LDS_AS const bf16x8*)(Ks + off.k[kk] + kb * 32 * (D * 2));
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[qt][kb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        s[qt][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[qt][kk], s[qt][kb], 0, 0, 0);
+}
+
+// mma_qk with NCOPY copy instructions of a later block placed between the
+// fragment reads in program order (the compiler keeps LDS-writing copies and
+// LDS reads in order, so this is where they issue): copy(i) is called after
+// read ((i+1) * NQ) / (NCOPY+1), spreading the texture-path work over the
+// MFMA stream instead of bursting it after the barrier.
+template <int D, int BN, int QT, int NCOPY, typename CopyFn>
+__device__ __forceinline__ void qk_block_with_copies(const char* Ks, const LdsOffsets<D>& off,
+                                                     const bf16x8 (&qf)[QT][D / 16],
+                                                     f32x16 (&s)[QT][BN / 32], CopyFn&& copy) {
+  constexpr int NKB = BN / 32;
+  constexpr int NQ = (D / 16) * NKB;
+  bf16x8 kf[D / 16][NKB];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int kk = i / NKB, kb = i % NKB;
+    kf[kk][kb] = *(LDS_AS const bf16x8*)(Ks + off.k[kk] + kb * 32 * (D * 2));
+#pragma unroll
+    for (int cidx = 0; cidx < NCOPY; ++cidx)
+      if (((cidx + 1) * NQ) / (NCOPY + 1) == i + 1) copy(cidx);
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -464,21 +528,32 @@ __device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
                                              const bf16x8 (&qf)[QT][D / 16],
                                              f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
                                              float (&l_run)[QT]) {
-  constexpr int PER_BLOCK = 2 * Tile<D, NW, BN>::LOADS;  // copy instructions per block per wave
-  if (j + ST - 2 < c.nblk)
-    wait_vmcnt<(ST - 2) * PER_BLOCK>();  // blocks j+1 .. j+ST-2 may stay in flight
-  else
-    wait_vmcnt<0>();
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
+  constexpr int PER_BLOCK = 2 * LD;  // copy instructions per block per wave
+  // every block issues its copies (past the last block a clamped duplicate
+  // lands in a free slot), so the count of younger copies is always exact
+  wait_vmcnt<(ST - 2) * PER_BLOCK>();  // blocks j+1 .. j+ST-2 may stay in flight
   __syncthreads();
-  if (j + ST - 1 < c.nblk) {
-    constexpr int NS = (SLOT + ST - 1) % ST;
-    issue_block_load<D, NW, BN, false>(c.Kh, (j + ST - 1) * BN, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane);
-    issue_block_load<D, NW, BN, true>(c.Vh, (j + ST - 1) * BN, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane);
-  }
+  constexpr int NS = (SLOT + ST - 1) % ST;
+  const int row_next = min(j + ST - 1, c.nblk - 1) * BN;
   const int kv0 = j * BN;
-  if (kv0 >= c.kv_end_w) return;  // wave-uniform: the whole block is masked for this wave
+  if (kv0 >= c.kv_end_w) {  // wave-uniform: the whole block is masked for this wave
+#pragma unroll
+    for (int t = 0; t < LD; ++t) {
+      issue_copy<D, NW, BN, false>(c.Kh, row_next, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
+      issue_copy<D, NW, BN, true>(c.Vh, row_next, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
+    }
+    return;
+  }
+  // copies of block j+ST-1 interleaved with the mma_qk stream of block j
   f32x16 s[QT][BN / 32];
-  qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, SLOT), off, qf, s);
+  qk_block_with_copies<D, BN, QT, PER_BLOCK>(k_slot<D, BN, ST>(smem, SLOT), off, qf, s, [&](int ci) {
+    const int t = ci >> 1;
+    if (ci & 1)
+      issue_copy<D, NW, BN, true>(c.Vh, row_next, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
+    else
+      issue_copy<D, NW, BN, false>(c.Kh, row_next, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
+  });
   sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
   if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
   bf16x8 pb[QT][BN / 16];
@@ -523,6 +598,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_simple(
     if (ST > 2 && j + 2 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 2 % ST>(c, smem, j + 2, off, qf, o, m_run, l_run);
     if (ST > 3 && j + 3 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 3 % ST>(c, smem, j + 3, off, qf, o, m_run, l_run);
   }
+  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
 
