@@ -46,6 +46,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "attn.h"
 
 namespace {
@@ -62,6 +64,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so
+// register arrays are only ever indexed by constants (never spilled to
+// scratch by a partially unrolled loop).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
 
 // NW waves, QT query tiles of 32 per wave, BN keys per block, ST ring slots.
 template <int D, int NW, int BN, int QT = 1, int ST = 2>
@@ -285,14 +302,13 @@ __device__ __forceinline__ void qk_block_with_copies(const char* Ks, const LdsOf
   constexpr int NKB = BN / 32;
   constexpr int NQ = (D / 16) * NKB;
   bf16x8 kf[D / 16][NKB];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int kk = i / NKB, kb = i % NKB;
-    kf[kk][kb] = *(LDS_AS const bf16x8*)(Ks + off.k[kk] + kb * 32 * (D * 2));
-#pragma unroll
-    for (int cidx = 0; cidx < NCOPY; ++cidx)
-      if (((cidx + 1) * NQ) / (NCOPY + 1) == i + 1) copy(cidx);
-  }
+  static_for<NQ>([&](auto I) {
+    constexpr int i = I;
+    kf[i / NKB][i % NKB] = *(LDS_AS const bf16x8*)(Ks + off.k[i / NKB] + (i % NKB) * 32 * (D * 2));
+    static_for<NCOPY>([&](auto C) {
+      if constexpr (((C + 1) * NQ) / (NCOPY + 1) == i + 1) copy(int(C));
+    });
+  });
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -564,8 +580,11 @@ __device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
   sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
 }
 
-template <int D, int NW, int BN, int QT, bool CAUSAL, int ST>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_simple(
+// OCC = workgroups per CU the register budget is sized for (waves per SIMD =
+// NW * OCC / 4): with NW = 4 and OCC = 2 two independent workgroups share a
+// CU, so the two waves on each SIMD are never held in step by one barrier.
+template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int OCC>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int negate_q) {
@@ -623,25 +642,38 @@ __device__ __forceinline__ void pipe_block(const Ctx& c, char* smem, int j, cons
                                            f32x16 (&s_cur)[QT][BN / 32],
                                            f32x16 (&s_nxt)[QT][BN / 32], f32x16 (&o)[QT][D / 32],
                                            float (&m_run)[QT], float (&l_run)[QT]) {
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
   wait_vmcnt<0>();
   __syncthreads();
-  if (j + 2 < c.nblk)
-    issue_block_load<D, NW, BN, false>(c.Kh, (j + 2) * BN, c.N, k_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane);
-  if (j + 1 < c.nblk)
-    issue_block_load<D, NW, BN, true>(c.Vh, (j + 1) * BN, c.N, v_slot<D, BN, 2>(smem, SLOT ^ 1), c.wave, c.lane);
+  // K_{j+2} over K_j (slot SLOT), V_{j+1} over V_{j-1} (slot SLOT^1); past the
+  // last block a clamped duplicate lands in a slot nobody reads again
+  const int row_k = min(j + 2, c.nblk - 1) * BN;
+  const int row_v = min(j + 1, c.nblk - 1) * BN;
+  auto copy = [&](int ci) {
+    const int t = ci >> 1;
+    if (ci & 1)
+      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, SLOT ^ 1), c.wave, c.lane, t);
+    else
+      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane, t);
+  };
   const int kv0 = j * BN;
-  if (kv0 >= c.kv_end_w) return;  // wave-uniform
+  const bool act = kv0 < c.kv_end_w;  // wave-uniform
   const bool nxt = kv0 + BN < c.kv_end_w;
   const bool msk = block_needs_mask<BN, CAUSAL>(c, kv0);
+  if (!act || !nxt) {
+#pragma unroll
+    for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
+    if (!act) return;
+  }
   bf16x8 pb[QT][BN / 16];
   float alpha[QT];
   if (nxt && !msk) {
-    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+    qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
     softmax_block<BN, QT>(s_cur, pb, c.c_log2, m_run, l_run, alpha);
     sched_mfma_with_reads_and_valu<(D / 16) * (BN / 32), 1, QT, kPfQK, 9>();
   } else {
     if (nxt) {
-      qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+      qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
       sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
     }
     if (msk) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
@@ -690,6 +722,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
     pipe_block<D, NW, BN, QT, CAUSAL, 0>(c, smem, j, off, qf, sa, sb, o, m_run, l_run);
     if (j + 1 < c.nblk) pipe_block<D, NW, BN, QT, CAUSAL, 1>(c, smem, j + 1, off, qf, sb, sa, o, m_run, l_run);
   }
+  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
 
@@ -710,21 +743,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
 // (B); at barrier 2m+1 the copies of K_{m+2} (over K_m) and V_{m+1} (over
 // V_{m-1}) start, and each wave waits for them before barrier 2m+3. Each
 // group runs its own loop; both pass the same number of barriers.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int VS, int KS>
+template <int D, int NW, int BN, int QT, bool CAUSAL, int VS, int KS, typename CopyFn>
 __device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int jp,
                                                    const LdsOffsets<D>& off,
                                                    const bf16x8 (&qf)[QT][D / 16],
                                                    f32x16 (&s)[QT][BN / 32],
                                                    const bf16x8 (&pb)[QT][BN / 16],
-                                                   f32x16 (&o)[QT][D / 32]) {
+                                                   f32x16 (&o)[QT][D / 32], int ncopy, CopyFn&& copy) {
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
   if (jp >= 0 && jp < c.nblk && jp * BN < c.kv_end_w) {
     pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, VS), off, pb, o);
     sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
   }
   const int jq = jp + 1;
   if (jq < c.nblk && jq * BN < c.kv_end_w) {
-    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, KS), off, qf, s);
+    if (ncopy)
+      qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, KS), off, qf, s, copy);
+    else
+      qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, KS), off, qf, s);
     sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
+  } else if (ncopy) {
+#pragma unroll
+    for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
   }
 }
 
@@ -743,16 +783,23 @@ __device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (
 }
 
 // Start of an odd interval t = 2m+1: every wave waits for its share of the
-// copies started two intervals ago, meets the others at the barrier, then
-// starts K_{m+2} (over K_m, slot MS) and V_{m+1} (over V_{m-1}, slot MS^1).
+// copies started two intervals ago and meets the others at the barrier; the
+// copies of K_{m+2} (over K_m, slot MS) and V_{m+1} (over V_{m-1}, slot MS^1)
+// are then issued by the returned functor, spread over the wave's next turn.
+// Past the last block a clamped duplicate lands in a slot nobody reads again.
 template <int D, int NW, int BN, int MS>
-__device__ __forceinline__ void pingpong_odd_barrier(const Ctx& c, char* smem, int m) {
+__device__ __forceinline__ auto pingpong_odd_barrier(const Ctx& c, char* smem, int m) {
   wait_vmcnt<0>();
   __syncthreads();
-  if (m + 2 < c.nblk)
-    issue_block_load<D, NW, BN, false>(c.Kh, (m + 2) * BN, c.N, k_slot<D, BN, 2>(smem, MS), c.wave, c.lane);
-  if (m + 1 < c.nblk)
-    issue_block_load<D, NW, BN, true>(c.Vh, (m + 1) * BN, c.N, v_slot<D, BN, 2>(smem, MS ^ 1), c.wave, c.lane);
+  const int row_k = min(m + 2, c.nblk - 1) * BN;
+  const int row_v = min(m + 1, c.nblk - 1) * BN;
+  return [&c, smem, row_k, row_v](int ci) {
+    const int t = ci >> 1;
+    if (ci & 1)
+      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, MS ^ 1), c.wave, c.lane, t);
+    else
+      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, 2>(smem, MS), c.wave, c.lane, t);
+  };
 }
 
 template <int D, int NW, int BN, int QT, bool CAUSAL>
@@ -786,6 +833,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pingpong(
   wait_vmcnt<0>();
   __syncthreads();
   const int n = c.nblk;
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
+  auto no_copy = [](int) {};
   // Both groups pass 2n+1 barriers after the prologue one.
   if (c.wave < NW / 2) {
     qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, s);  // S_0 (block 0 is never skipped)
@@ -794,13 +843,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pingpong(
       // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
       __syncthreads();
       pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
-      pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o);
+      {
+        auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
+        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 1, copy);
+      }
       if (j + 1 < n) {  // block j+1 (odd): slots swap
         __syncthreads();
         pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
-        pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
-        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o);
+        auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
+        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o, 1, copy);
       }
     }
     __syncthreads();  // t = 2n: group B's last mma_pv
@@ -808,22 +859,29 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pingpong(
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] pv(j-1) from V slot 1, qk(j) from K slot 0 | [t=2j+1] softmax
       __syncthreads();
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o);
-      pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o, 0, no_copy);
+      {
+        auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
+#pragma unroll
+        for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
+      }
       pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
       if (j + 1 < n) {
         __syncthreads();
-        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o);
-        pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
+        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 0, no_copy);
+        auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
+#pragma unroll
+        for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
         pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
       }
     }
     __syncthreads();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
     if (n & 1)
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, n - 1, off, qf, s, pb, o);
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, n - 1, off, qf, s, pb, o, 0, no_copy);
     else
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, n - 1, off, qf, s, pb, o);
+      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, n - 1, off, qf, s, pb, o, 0, no_copy);
   }
+  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
 
@@ -834,7 +892,7 @@ typedef hipError_t (*launch_fn)(const void*, const void*, const void*, float*, f
 
 enum Schedule { kSimple = 0, kPipelined = 1, kPingPong = 2 };
 
-template <int D, int NW, int BN, int QT, int SCHED, int ST>
+template <int D, int NW, int BN, int QT, int SCHED, int ST, int OCC = 1>
 hipError_t launch(const void* q, const void* k, const void* v, float* out, float* lse, int B,
                   int H, int N, int causal, float scale, hipStream_t stream) {
   using T = Tile<D, NW, BN, QT, ST>;
@@ -856,9 +914,9 @@ hipError_t launch(const void* q, const void* k, const void* v, float* out, float
       hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else {
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
     else
-      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, false, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, false, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   }
   return hipGetLastError();
 }
@@ -869,39 +927,42 @@ struct Variant {
   launch_fn fn;
 };
 
-#define VARIANT(NAME, D, NW, BN, QT, SCHED, ST)                                        \
+#define VARIANT(NAME, D, NW, BN, QT, SCHED, ST, OCC)                                   \
   Variant {                                                                            \
     NAME, D, 32 * QT * NW, BN, NW, Tile<D, NW, BN, QT, ST>::LDS_BYTES,                 \
-        &launch<D, NW, BN, QT, SCHED, ST>                                              \
+        &launch<D, NW, BN, QT, SCHED, ST, OCC>                                         \
   }
 
 // Name fields: head dim, query rows per workgroup, keys per block, waves,
-// query tiles per wave, LDS ring slots, schedule.
+// query tiles per wave, LDS ring slots, workgroups per CU (occ), schedule.
 const Variant kVariants[] = {
-    VARIANT("d64_bm256_bn64_w8_q1_st2_simple", 64, 8, 64, 1, kSimple, 2),         // 0
-    VARIANT("d128_bm256_bn64_w8_q1_st2_simple", 128, 8, 64, 1, kSimple, 2),       // 1
-    VARIANT("d256_bm128_bn64_w4_q1_st2_simple", 256, 4, 64, 1, kSimple, 2),       // 2
-    VARIANT("d64_bm256_bn64_w4_q2_st2_pipe", 64, 4, 64, 2, kPipelined, 2),        // 3
-    VARIANT("d128_bm256_bn64_w4_q2_st2_pipe", 128, 4, 64, 2, kPipelined, 2),      // 4
-    VARIANT("d128_bm256_bn64_w8_q1_st2_pingpong", 128, 8, 64, 1, kPingPong, 2),   // 5
-    VARIANT("d64_bm256_bn64_w8_q1_st2_pingpong", 64, 8, 64, 1, kPingPong, 2),     // 6
-    VARIANT("d128_bm256_bn64_w4_q2_st2_simple", 128, 4, 64, 2, kSimple, 2),       // 7
-    VARIANT("d128_bm128_bn64_w4_q1_st2_pipe", 128, 4, 64, 1, kPipelined, 2),      // 8
-    VARIANT("d256_bm128_bn64_w4_q1_st2_pipe", 256, 4, 64, 1, kPipelined, 2),      // 9
-    VARIANT("d128_bm256_bn64_w8_q1_st4_simple", 128, 8, 64, 1, kSimple, 4),       // 10
-    VARIANT("d128_bm256_bn32_w8_q1_st2_simple", 128, 8, 32, 1, kSimple, 2),       // 11
-    VARIANT("d128_bm256_bn32_w4_q2_st2_pipe", 128, 4, 32, 2, kPipelined, 2),      // 12
-    VARIANT("d64_bm128_bn32_w4_q1_st2_simple", 64, 4, 32, 1, kSimple, 2),         // 13
-    VARIANT("d64_bm256_bn32_w4_q2_st2_pipe", 64, 4, 32, 2, kPipelined, 2),        // 14
-    VARIANT("d128_bm256_bn32_w4_q2_st2_simple", 128, 4, 32, 2, kSimple, 2),       // 15
+    VARIANT("d64_bm256_bn64_w8_q1_st2_occ1_simple", 64, 8, 64, 1, kSimple, 2, 1),         // 0
+    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_simple", 128, 8, 64, 1, kSimple, 2, 1),       // 1
+    VARIANT("d256_bm128_bn64_w4_q1_st2_occ1_simple", 256, 4, 64, 1, kSimple, 2, 1),       // 2
+    VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_simple", 128, 4, 64, 1, kSimple, 2, 2),       // 3
+    VARIANT("d64_bm128_bn64_w4_q1_st2_occ2_simple", 64, 4, 64, 1, kSimple, 2, 2),         // 4
+    VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_simple", 64, 4, 64, 1, kSimple, 2, 3),         // 5
+    VARIANT("d256_bm128_bn32_w4_q1_st2_occ2_simple", 256, 4, 32, 1, kSimple, 2, 2),       // 6
+    VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_simple", 256, 4, 32, 1, kSimple, 2, 1),       // 7
+    VARIANT("d128_bm128_bn64_w4_q1_st3_occ2_simple", 128, 4, 64, 1, kSimple, 3, 2),       // 8
+    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pingpong", 128, 8, 64, 1, kPingPong, 2, 1),   // 9
+    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pipe", 128, 8, 64, 1, kPipelined, 2, 1),      // 10
+    VARIANT("d64_bm256_bn64_w8_q1_st2_occ1_pipe", 64, 8, 64, 1, kPipelined, 2, 1),        // 11
+    VARIANT("d128_bm256_bn64_w4_q2_st2_occ1_simple", 128, 4, 64, 2, kSimple, 2, 1),       // 12
+    VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_simple", 128, 8, 32, 1, kSimple, 2, 1),       // 13
+    VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_pipe", 128, 8, 32, 1, kPipelined, 2, 1),      // 14
+    VARIANT("d64_bm128_bn32_w4_q1_st2_occ1_simple", 64, 4, 32, 1, kSimple, 2, 1),         // 15
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
+// Measured choice per (head dim, mask) on MI355X: the 8-wave ping-pong
+// schedule for long non-causal d = 128; 4-wave 128-row workgroups at two or three per
+// CU where causal work is short or VALU-heavy (more, independent
+// workgroups); 4-wave workgroups for d = 256 (O alone takes 128 registers).
 int default_variant(int d, int causal) {
-  (void)causal;
   switch (d) {
-    case 64: return 0;
-    case 128: return 1;
+    case 64: return 5;
+    case 128: return causal ? 3 : 9;
     case 256: return 2;
     default: return -1;
   }

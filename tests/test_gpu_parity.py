@@ -199,7 +199,7 @@ def test_overlapped_schedules_match_simple_schedule_bitwise():
     for i in range(attn.attn_num_variants()):
         info = attn.attn_variant_info(i)
         name = attn.attn_variant_name(i)
-        if name.endswith("_st2_simple"):
+        if "_st2_" in name and name.endswith("_simple"):
             refs.setdefault((info["head_dim"], info["block_n"]), i)
     for i in range(attn.attn_num_variants()):
         info = attn.attn_variant_info(i)
