@@ -222,24 +222,6 @@ __device__ __forceinline__ void sched_mfma_with_reads() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
 }
-// As above, with NVM copy instructions (0x020 VMEM read) spread evenly over
-// the MFMA stream so the texture path never sees a burst.
-template <int I, int STEPS, int RD, int MR, int NVM>
-__device__ __forceinline__ void sched_copy_steps() {
-  if constexpr (I < STEPS) {
-    __builtin_amdgcn_sched_group_barrier(0x008, MR, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-    constexpr int due = ((I + 1) * NVM) / STEPS - (I * NVM) / STEPS;
-    if constexpr (due > 0) __builtin_amdgcn_sched_group_barrier(0x010, due, 0);
-    sched_copy_steps<I + 1, STEPS, RD, MR, NVM>();
-  }
-}
-template <int NR, int RD, int MR, int PF, int NVM>
-__device__ __forceinline__ void sched_mfma_with_reads_and_copies() {
-  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
-  sched_copy_steps<0, NR - PF, RD, MR, NVM>();
-  __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
-}
 template <int NR, int RD, int MR, int PF, int NV>
 __device__ __forceinline__ void sched_mfma_with_reads_and_valu() {
   __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
@@ -257,6 +239,36 @@ __device__ __forceinline__ void sched_mfma_with_reads_and_valu() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
   }
+}
+
+// Pin a value's computation before this point (an empty asm that "uses" it):
+// keeps the compiler from sinking overlapped softmax work out of the MFMA
+// stream it was scheduled into.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Copies interleaved with an MFMA stream of NR read groups whose reads run PF
+// groups ahead: copy c of NC is issued in steady step (c * (NR - PF)) / NC,
+// right after that step's reads (read group PF + step); a stream with no
+// steady part (NR <= PF) issues them all after its last read. The stream's
+// program order and its scheduling pattern both use this placement, so the
+// compiler (which keeps LDS-writing copies and LDS reads in order) can honour
+// both.
+template <int NR, int PF, int NC>
+constexpr int copy_step(int c) {
+  return (c * (NR - PF)) / NC;
+}
+template <int NR, int PF, int NC>
+constexpr int copy_after_group(int c) {
+  return NR > PF ? PF + copy_step<NR, PF, NC>(c) : NR - 1;
+}
+template <int NR, int PF, int NC>
+constexpr int copies_due(int step) {
+  int n = 0;
+  for (int c = 0; c < NC; ++c) n += copy_step<NR, PF, NC>(c) == step;
+  return n;
 }
 
 constexpr int kPfQK = 4;  // K fragments in flight ahead of mma_qk
@@ -291,10 +303,9 @@ __device__ __forceinline__ void qk_block(const char* Ks, const LdsOffsets<D>& of
 }
 
 // mma_qk with NCOPY copy instructions of a later block placed between the
-// fragment reads in program order (the compiler keeps LDS-writing copies and
-// LDS reads in order, so this is where they issue): copy(i) is called after
-// read ((i+1) * NQ) / (NCOPY+1), spreading the texture-path work over the
-// MFMA stream instead of bursting it after the barrier.
+// fragment reads in program order at the copy_step positions, spreading the
+// texture-path work over the MFMA stream instead of bursting it after the
+// barrier.
 template <int D, int BN, int QT, int NCOPY, typename CopyFn>
 __device__ __forceinline__ void qk_block_with_copies(const char* Ks, const LdsOffsets<D>& off,
                                                      const bf16x8 (&qf)[QT][D / 16],
@@ -306,7 +317,8 @@ __device__ __forceinline__ void qk_block_with_copies(const char* Ks, const LdsOf
     constexpr int i = I;
     kf[i / NKB][i % NKB] = *(LDS_AS const bf16x8*)(Ks + off.k[i / NKB] + (i % NKB) * 32 * (D * 2));
     static_for<NCOPY>([&](auto C) {
-      if constexpr (((C + 1) * NQ) / (NCOPY + 1) == i + 1) copy(int(C));
+      static_assert(copy_after_group<NQ, kPfQK, NCOPY>(C) < NQ, "every copy is placed");
+      if constexpr (copy_after_group<NQ, kPfQK, NCOPY>(C) == i) copy(int(C));
     });
   });
 #pragma unroll
@@ -340,48 +352,90 @@ __device__ __forceinline__ void mask_block(f32x16 (&s)[QT][BN / 32], int kv0, in
       }
 }
 
-// softmax (per query tile): new running max, alpha = exp2(m_old - m_new),
-// p = exp2(c*s - m) with the row sum taken from fp32 p, and P^T packed to
-// bf16 (RNE) as the B operand of mma_pv: pb[qt][2*kb + hf] holds accumulator
-// registers 8*hf..8*hf+7 of key tile kb. alpha is 1 exactly when a row's max
-// did not move.
+// softmax (per query tile), in three pieces so that overlapped schedules can
+// spread it over MFMA streams; every schedule runs the same pieces in the
+// same order, so results agree bit for bit:
+//   softmax_stats: new running max (exact: max has no rounding, so the order
+//                  of the max tree is free), alpha = exp2(m_old - m_new)
+//                  (1 exactly when the max did not move, 0 on the first
+//                  block);
+//   softmax_exp<KB>: p = exp2(c*s - m) for key tile KB, written over the
+//                  scores, with the row sum taken from fp32 p (tile 0 first,
+//                  registers in order);
+//   softmax_pack:  P^T to bf16 (RNE) as the B operand of mma_pv:
+//                  pb[qt][2*kb + hf] holds accumulator registers 8*hf..8*hf+7
+//                  of key tile kb;
+//   softmax_sum:   l = l * alpha + (ps0 + ps1) + (ps2 + ps3).
 template <int BN, int QT>
-__device__ __forceinline__ void softmax_block(const f32x16 (&s)[QT][BN / 32],
-                                              bf16x8 (&pb)[QT][BN / 16], float c_log2,
-                                              float (&m_run)[QT], float (&l_run)[QT],
-                                              float (&alpha)[QT]) {
+__device__ __forceinline__ void softmax_stats(const f32x16 (&s)[QT][BN / 32], float c_log2,
+                                              float (&m_run)[QT], float (&alpha)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // two chains of 3-input maxima over the lane's 16 * BN/32 scores
+    float mx[2];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      constexpr int NV = 16 * (BN / 32) / 2;
+      auto v = [&](int i) { const int g = h2 * NV + i; return s[qt][g / 16][g % 16]; };
+      float m = fmaxf(v(0), fmaxf(v(1), v(2)));
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const int c = (r >> 2) & 3;
-        mx[c] = fmaxf(mx[c], fmaxf(s[qt][kb][r], s[qt][kb][r + 1]));
-        mx[c] = fmaxf(mx[c], fmaxf(s[qt][kb][r + 2], s[qt][kb][r + 3]));
-      }
-    float bmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    bmax = swap32_max(bmax);
+      for (int i = 3; i + 1 < NV; i += 2) m = fmaxf(m, fmaxf(v(i), v(i + 1)));
+      if constexpr (NV % 2 == 0) m = fmaxf(m, v(NV - 1));
+      mx[h2] = m;
+    }
+    const float bmax = swap32_max(fmaxf(mx[0], mx[1]));
     const float m_new = fmaxf(m_run[qt], bmax * c_log2);
-    alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 on the first block
+    alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
     m_run[qt] = m_new;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kb][8 * hf + e], c_log2, -m_new));
-          pv[e] = p;
-          ps[e & 3] += p;
-        }
-        pb[qt][2 * kb + hf] = __builtin_convertvector(pv, bf16x8);
-      }
-    l_run[qt] = __builtin_fmaf(l_run[qt], alpha[qt], (ps[0] + ps[1]) + (ps[2] + ps[3]));
   }
+}
+
+template <int BN, int QT, int KB>
+__device__ __forceinline__ void softmax_exp(f32x16 (&s)[QT][BN / 32], float c_log2,
+                                            const float (&m_run)[QT], float (&ps)[QT][4]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][KB][r], c_log2, -m_run[qt]));
+      s[qt][KB][r] = p;  // in place: the score is dead once its weight exists
+      // the first four terms start the four partial sums (0 + p == p exactly)
+      if (KB == 0 && r < 4) ps[qt][r] = p;
+      else ps[qt][r & 3] += p;
+    }
+}
+
+template <int BN, int QT>
+__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      pb[qt][2 * kb] = __builtin_convertvector(
+          __builtin_shufflevector(s[qt][kb], s[qt][kb], 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
+      pb[qt][2 * kb + 1] = __builtin_convertvector(
+          __builtin_shufflevector(s[qt][kb], s[qt][kb], 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+    }
+}
+
+template <int QT>
+__device__ __forceinline__ void softmax_sum(float (&l_run)[QT], const float (&alpha)[QT],
+                                            const float (&ps)[QT][4]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+    l_run[qt] = __builtin_fmaf(l_run[qt], alpha[qt], (ps[qt][0] + ps[qt][1]) + (ps[qt][2] + ps[qt][3]));
+}
+
+// All of softmax for one block; S is overwritten with P (fp32).
+template <int BN, int QT>
+__device__ __forceinline__ void softmax_block(f32x16 (&s)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16],
+                                              float c_log2, float (&m_run)[QT], float (&l_run)[QT],
+                                              float (&alpha)[QT]) {
+  float ps[QT][4];
+  softmax_stats<BN, QT>(s, c_log2, m_run, alpha);
+  static_for<BN / 32>([&](auto KB) { softmax_exp<BN, QT, KB>(s, c_log2, m_run, ps); });
+  softmax_pack<BN, QT>(s, pb);
+  softmax_sum<QT>(l_run, alpha, ps);
 }
 
 // rescale: O *= alpha, skipped by the whole wave when no row moved its max.
@@ -479,7 +533,7 @@ struct Ctx {
   const uint16_t* Vh;
   size_t head;
   int bh;
-  int N, nblk, kv_end_w, q0w, qi0, wave, lane;
+  int N, nblk, kv_end_w, q0, q0w, qi0, wave, lane;
   float c_log2;
 };
 
@@ -495,6 +549,7 @@ __device__ __forceinline__ Ctx make_ctx(const uint16_t* K, const uint16_t* V, in
   const int tq = L % n_qtiles;
   const int tile = CAUSAL ? (n_qtiles - 1 - tq) : tq;
   const int q0 = tile * BM;
+  c.q0 = q0;
   c.q0w = q0 + c.wave * WROWS;
   c.qi0 = c.q0w + (c.lane & 31);
   c.head = (size_t)c.bh * N * D;
@@ -625,67 +680,159 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
 // Software-pipelined schedule inside each wave (the pages' FlashAttention-
 // forward schedule found by Twill, section 3.1 of the software-pipelining
 // page: the first GEMM is hoisted into the loop prologue so exp latency is
-// never exposed, and one tile's exp overlaps another tile's GEMM; restated
-// for gfx950, where one wave interleaving its own MFMAs and VALU keeps both
-// units busy):
-//   prologue : K_0, V_0, K_1 -> LDS; S_0 = Q K_0^T
-//   block j  : copies of K_{j+2}, V_{j+1} in flight (one barrier per block)
-//              while the wave issues mma_qk(K_{j+1}) and, between those
-//              MFMAs, the softmax of S_j; then rescale and mma_pv(V_j).
-// K runs two blocks ahead of its use and V one; LDS holds two K and two V
-// slots. At the top of block j each wave waits for K_{j+1} and V_j; after the
-// barrier K_j (read by mma_qk in block j-1) and V_{j-1} (read by mma_pv in
-// block j-1) are free.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int SLOT>
-__device__ __forceinline__ void pipe_block(const Ctx& c, char* smem, int j, const LdsOffsets<D>& off,
-                                           const bf16x8 (&qf)[QT][D / 16],
-                                           f32x16 (&s_cur)[QT][BN / 32],
-                                           f32x16 (&s_nxt)[QT][BN / 32], f32x16 (&o)[QT][D / 32],
-                                           float (&m_run)[QT], float (&l_run)[QT]) {
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
+// never exposed, and one tile's softmax overlaps the other GEMMs), restated
+// for gfx950. A wave issues at most about one VALU instruction per two VALU
+// issue slots of its SIMD, while its MFMAs run alongside its own VALU work,
+// so every phase here gives each wave both kinds of work and both waves of a
+// SIMD keep the matrix core busy together:
+//   prologue : K_0, K_1 -> LDS; S_0 = Q K_0^T
+//   block j  : (a) mma_pv(V_{j-1}, P_{j-1})  with  mask, max and exp of the
+//                  first key tile of S_j;
+//              (b) mma_qk(K_{j+1}) -> S_{j+1}  with  exp of the other key
+//                  tiles, row sum and packing of P_j;
+//              then O *= alpha_j (skipped when no row's max moved)
+//   epilogue : mma_pv(V_{n-1}, P_{n-1})
+// O sees exactly the simple schedule's sequence of updates (... += P_{j-1}V,
+// *= alpha_j, += P_j V ...), so results agree bit for bit. LDS holds two K
+// and two V slots; at the top of block j each wave waits for K_{j+1} and
+// V_{j-1}, meets the others at the barrier (after which K_j and V_{j-2} are
+// no longer read) and, spread through phase (b), copies K_{j+2} over K_j and
+// V_j over V_{j-2}.
+
+// MFMA stream of NR read groups (RD reads each, feeding MR MFMAs) with NV
+// VALU instructions after every MFMA and NVM VMEM copies spread over the
+// steady part; reads run PF groups ahead.
+template <int I, int NR, int PF, int RD, int MR, int NV, int NVM>
+__device__ __forceinline__ void sched_valu_steps() {
+  if constexpr (I < NR - PF) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    constexpr int due = copies_due<NR, PF, NVM>(I);
+    if constexpr (due > 0) __builtin_amdgcn_sched_group_barrier(0x010, due, 0);
+    sched_valu_steps<I + 1, NR, PF, RD, MR, NV, NVM>();
+  }
+}
+template <int NR, int RD, int MR, int PF, int NV, int NVM>
+__device__ __forceinline__ void sched_mfma_reads_valu_copies() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
+  sched_valu_steps<0, NR, PF, RD, MR, NV, NVM>();
+#pragma unroll
+  for (int i = 0; i < PF * MR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
+// Top of block j: wait for this wave's copies of K_{j+1} and V_{j-1}, meet
+// the others (K_j and V_{j-2} are then free) and return the functor that
+// copies K_{j+2} over K_j and V_j over V_{j-2} (slot SLOT of each ring); past
+// the last block a clamped duplicate lands in a slot nobody reads again.
+template <int D, int NW, int BN, int SLOT>
+__device__ __forceinline__ auto pipe_top(const Ctx& c, char* smem, int j) {
   wait_vmcnt<0>();
   __syncthreads();
-  // K_{j+2} over K_j (slot SLOT), V_{j+1} over V_{j-1} (slot SLOT^1); past the
-  // last block a clamped duplicate lands in a slot nobody reads again
   const int row_k = min(j + 2, c.nblk - 1) * BN;
-  const int row_v = min(j + 1, c.nblk - 1) * BN;
-  auto copy = [&](int ci) {
+  const int row_v = j * BN;
+  return [&c, smem, row_k, row_v](int ci) {
     const int t = ci >> 1;
     if (ci & 1)
-      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, SLOT ^ 1), c.wave, c.lane, t);
+      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane, t);
     else
       issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane, t);
   };
-  const int kv0 = j * BN;
-  const bool act = kv0 < c.kv_end_w;  // wave-uniform
-  const bool nxt = kv0 + BN < c.kv_end_w;
-  const bool msk = block_needs_mask<BN, CAUSAL>(c, kv0);
-  if (!act || !nxt) {
-#pragma unroll
-    for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
-    if (!act) return;
-  }
-  bf16x8 pb[QT][BN / 16];
-  float alpha[QT];
-  if (nxt && !msk) {
-    qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
-    softmax_block<BN, QT>(s_cur, pb, c.c_log2, m_run, l_run, alpha);
-    sched_mfma_with_reads_and_valu<(D / 16) * (BN / 32), 1, QT, kPfQK, 9>();
-  } else {
-    if (nxt) {
-      qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
-      sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
-    }
-    if (msk) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
-    softmax_block<BN, QT>(s_cur, pb, c.c_log2, m_run, l_run, alpha);
-  }
-  rescale_block<D, QT>(o, alpha);
-  pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT), off, pb, o);
-  sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
 }
 
-template <int D, int NW, int BN, int QT, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
+// Block j when the whole workgroup has P_{j-1}, an unmasked S_j and a next
+// block: both phases overlapped.
+template <int D, int NW, int BN, int QT, int SLOT>
+__device__ __forceinline__ void pipe_block_fast(const Ctx& c, char* smem, int j, const LdsOffsets<D>& off,
+                                                const bf16x8 (&qf)[QT][D / 16],
+                                                f32x16 (&s_cur)[QT][BN / 32],
+                                                f32x16 (&s_nxt)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16],
+                                                f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
+                                                float (&l_run)[QT]) {
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
+  constexpr int NB = BN / 32;
+  auto copy = pipe_top<D, NW, BN, SLOT>(c, smem, j);
+  float alpha[QT], ps[QT][4];
+  // (a) mma_pv(V_{j-1}) with max and exp of key tile 0
+  pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT ^ 1), off, pb, o);
+  softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
+  softmax_exp<BN, QT, 0>(s_cur, c.c_log2, m_run, ps);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    pin(s_cur[qt][0]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pin(ps[qt][e]);
+  }
+  sched_mfma_reads_valu_copies<(BN / 16) * (D / 32), 2, QT, kPfPV, 5, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // (b) mma_qk(K_{j+1}) with this block's copies, the remaining exps, row sum
+  // and packing. (Copies sit among the K reads: plain LDS loads whose
+  // addresses the compiler can tell apart from the copy destinations; next to
+  // the transposing V reads it would wait for every copy to land.)
+  qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
+  static_for<NB - 1>([&](auto KB) { softmax_exp<BN, QT, KB + 1>(s_cur, c.c_log2, m_run, ps); });
+  softmax_sum<QT>(l_run, alpha, ps);
+  softmax_pack<BN, QT>(s_cur, pb);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    pin(l_run[qt]);
+#pragma unroll
+    for (int p = 0; p < BN / 16; ++p) pin(pb[qt][p]);
+  }
+  sched_mfma_reads_valu_copies<(D / 16) * NB, 1, QT, kPfQK, 4, 2 * LD>();
+  __builtin_amdgcn_sched_barrier(0);
+  rescale_block<D, QT>(o, alpha);
+}
+
+// Any block (first, masked, past a wave's causal limit, last): the same
+// steps in the same order, without overlap.
+template <int D, int NW, int BN, int QT, bool CAUSAL, int SLOT>
+__device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int j,
+                                                   const LdsOffsets<D>& off,
+                                                   const bf16x8 (&qf)[QT][D / 16],
+                                                   f32x16 (&s_cur)[QT][BN / 32],
+                                                   f32x16 (&s_nxt)[QT][BN / 32],
+                                                   bf16x8 (&pb)[QT][BN / 16], f32x16 (&o)[QT][D / 32],
+                                                   float (&m_run)[QT], float (&l_run)[QT]) {
+  constexpr int LD = Tile<D, NW, BN>::LOADS;
+  constexpr int NB = BN / 32;
+  auto copy = pipe_top<D, NW, BN, SLOT>(c, smem, j);
+#pragma unroll
+  for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
+  const int kv0 = j * BN;
+  const bool act = kv0 < c.kv_end_w;                         // S_j has live keys (wave-uniform)
+  const bool prv = j > 0 && kv0 - BN < c.kv_end_w;           // P_{j-1} exists
+  const bool nxt = j + 1 < c.nblk && kv0 + BN < c.kv_end_w;  // S_{j+1} is needed
+  float alpha[QT], ps[QT][4];
+  if (prv) {
+    pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT ^ 1), off, pb, o);
+    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
+  }
+  if (act) {
+    if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
+    softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
+    softmax_exp<BN, QT, 0>(s_cur, c.c_log2, m_run, ps);
+  }
+  if (nxt) {
+    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+    sched_mfma_with_reads<(D / 16) * NB, 1, QT, kPfQK>();
+  }
+  if (act) {
+    static_for<NB - 1>([&](auto KB) { softmax_exp<BN, QT, KB + 1>(s_cur, c.c_log2, m_run, ps); });
+    softmax_sum<QT>(l_run, alpha, ps);
+    softmax_pack<BN, QT>(s_cur, pb);
+    rescale_block<D, QT>(o, alpha);
+  }
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipelined(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int negate_q) {
@@ -693,11 +840,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
 
-  // prologue: Q; K_0, V_0, K_1 in flight; S_0 = Q K_0^T
+  // prologue: Q; K_0, K_1 in flight; S_0 = Q K_0^T
   bf16x8 qf[QT][D / 16];
   load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
   issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
-  issue_block_load<D, NW, BN, true>(c.Vh, 0, N, v_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
   if (c.nblk > 1)
     issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
   const LdsOffsets<D> off(c.lane);
@@ -711,18 +857,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_pipelined(
     l_run[qt] = 0.f;
   }
   f32x16 sa[QT][BN / 32], sb[QT][BN / 32];
+  bf16x8 pb[QT][BN / 16];
   wait_vmcnt<0>();
   __syncthreads();
   qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, sa);  // block 0 is never skipped
   sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
 
-  // two blocks per trip so S_cur / S_next swap roles without register copies
-  // and every LDS slot offset is an immediate
-  for (int j = 0; j < c.nblk; j += 2) {
-    pipe_block<D, NW, BN, QT, CAUSAL, 0>(c, smem, j, off, qf, sa, sb, o, m_run, l_run);
-    if (j + 1 < c.nblk) pipe_block<D, NW, BN, QT, CAUSAL, 1>(c, smem, j + 1, off, qf, sb, sa, o, m_run, l_run);
+  // Blocks 1 .. jf-1 take the overlapped path for every wave: they have a
+  // previous and a next block, no key past N and (causal) no key past the
+  // workgroup's first query. Block 0 and blocks jf .. n-1 take the generic
+  // path. Slot and S roles alternate with the block parity.
+  const int n = c.nblk;
+  int jf = n - 1;
+  if (N % BN) jf = min(jf, N / BN);
+  if (CAUSAL) jf = min(jf, (c.q0 + 1) / BN);
+  pipe_block_generic<D, NW, BN, QT, CAUSAL, 0>(c, smem, 0, off, qf, sa, sb, pb, o, m_run, l_run);
+  int j = 1;
+  for (; j + 1 < jf; j += 2) {
+    pipe_block_fast<D, NW, BN, QT, 1>(c, smem, j, off, qf, sb, sa, pb, o, m_run, l_run);
+    pipe_block_fast<D, NW, BN, QT, 0>(c, smem, j + 1, off, qf, sa, sb, pb, o, m_run, l_run);
   }
-  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+  for (; j < n; j += 2) {
+    pipe_block_generic<D, NW, BN, QT, CAUSAL, 1>(c, smem, j, off, qf, sb, sa, pb, o, m_run, l_run);
+    if (j + 1 < n) pipe_block_generic<D, NW, BN, QT, CAUSAL, 0>(c, smem, j + 1, off, qf, sa, sb, pb, o, m_run, l_run);
+  }
+  // epilogue: mma_pv of the last block (V_{n-1} copied during block n-1)
+  wait_vmcnt<0>();
+  __syncthreads();
+  if ((n - 1) * BN < c.kv_end_w) {
+    if ((n - 1) & 1) pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, 1), off, pb, o);
+    else pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, 0), off, pb, o);
+  }
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
 
@@ -802,8 +967,8 @@ __device__ __forceinline__ auto pingpong_odd_barrier(const Ctx& c, char* smem, i
   };
 }
 
-template <int D, int NW, int BN, int QT, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_pingpong(
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int negate_q) {
@@ -904,14 +1069,14 @@ hipError_t launch(const void* q, const void* k, const void* v, float* out, float
   const dim3 grid((unsigned)G), block(NW * 64);
   if constexpr (SCHED == kPingPong) {
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
     else
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else if constexpr (SCHED == kPipelined) {
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
     else
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else {
     if (causal)
       hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
