@@ -1117,6 +1117,12 @@ const Variant kVariants[] = {
     VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_simple", 128, 8, 32, 1, kSimple, 2, 1),       // 13
     VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_pipe", 128, 8, 32, 1, kPipelined, 2, 1),      // 14
     VARIANT("d64_bm128_bn32_w4_q1_st2_occ1_simple", 64, 4, 32, 1, kSimple, 2, 1),         // 15
+    VARIANT("d128_bm256_bn128_w8_q1_st2_occ1_pingpong", 128, 8, 128, 1, kPingPong, 2, 1), // 16
+    VARIANT("d128_bm256_bn128_w8_q1_st2_occ1_simple", 128, 8, 128, 1, kSimple, 2, 1),     // 17
+    VARIANT("d256_bm128_bn64_w4_q1_st2_occ1_pipe", 256, 4, 64, 1, kPipelined, 2, 1),      // 18
+    VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_pipe", 64, 4, 64, 1, kPipelined, 2, 3),        // 19
+    VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_pipe", 128, 4, 64, 1, kPipelined, 2, 2),      // 20
+    VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_pipe", 256, 4, 32, 1, kPipelined, 2, 1),      // 21
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1127,7 +1133,7 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 int default_variant(int d, int causal) {
   switch (d) {
     case 64: return 5;
-    case 128: return causal ? 3 : 9;
+    case 128: return causal ? 3 : 16;
     case 256: return 2;
     default: return -1;
   }
