@@ -1123,6 +1123,7 @@ const Variant kVariants[] = {
     VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_pipe", 64, 4, 64, 1, kPipelined, 2, 3),        // 19
     VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_pipe", 128, 4, 64, 1, kPipelined, 2, 2),      // 20
     VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_pipe", 256, 4, 32, 1, kPipelined, 2, 1),      // 21
+    VARIANT("d64_bm128_bn128_w4_q1_st2_occ2_simple", 64, 4, 128, 1, kSimple, 2, 2),       // 22
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1132,7 +1133,7 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // workgroups); 4-wave workgroups for d = 256 (O alone takes 128 registers).
 int default_variant(int d, int causal) {
   switch (d) {
-    case 64: return 5;
+    case 64: return 22;
     case 128: return causal ? 3 : 16;
     case 256: return 2;
     default: return -1;
