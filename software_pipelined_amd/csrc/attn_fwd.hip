@@ -273,6 +273,7 @@ constexpr int copies_due(int step) {
 
 constexpr int kPfQK = 4;  // K fragments in flight ahead of mma_qk
 constexpr int kPfPV = 2;  // V fragment pairs in flight ahead of mma_pv
+constexpr int kPfPVTurn = 3;  // the same for a ping-pong matrix turn (one wave streams alone)
 
 // mma_qk: S^T[key][query] for BN keys (K block image at Ks) against the
 // wave's QT query tiles. A operand = K rows (ds_read_b128), B operand = Q^T.
@@ -916,9 +917,12 @@ __device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int
                                                    const bf16x8 (&pb)[QT][BN / 16],
                                                    f32x16 (&o)[QT][D / 32], int ncopy, CopyFn&& copy) {
   constexpr int LD = Tile<D, NW, BN>::LOADS;
+  // the wave on the matrix core issues ahead of the wave in its softmax turn
+  // (measured: +2% over equal priority, -2% with the priorities reversed)
+  __builtin_amdgcn_s_setprio(1);
   if (jp >= 0 && jp < c.nblk && jp * BN < c.kv_end_w) {
     pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, VS), off, pb, o);
-    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
+    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPVTurn>();
   }
   const int jq = jp + 1;
   if (jq < c.nblk && jq * BN < c.kv_end_w) {
@@ -938,6 +942,7 @@ __device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (
                                                    bf16x8 (&pb)[QT][BN / 16],
                                                    f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
                                                    float (&l_run)[QT]) {
+  __builtin_amdgcn_s_setprio(0);
   if (j < c.nblk && j * BN < c.kv_end_w) {
     const int kv0 = j * BN;
     if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
