@@ -372,19 +372,21 @@ __device__ __forceinline__ void softmax_stats(const f32x16 (&s)[QT][BN / 32], fl
                                               float (&m_run)[QT], float (&alpha)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    // two chains of 3-input maxima over the lane's 16 * BN/32 scores
-    float mx[2];
+    // four left-deep chains over the lane's 16 * BN/32 scores, written so
+    // that each step folds two new scores (one v_max3_f32); pairwise maxima
+    // would cost 1.5x the instructions
+    constexpr int NCH = 4, NV = 16 * (BN / 32) / NCH;
+    static_assert(NV >= 3 && NV % 2 == 0, "chain length");
+    float mx[NCH];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      constexpr int NV = 16 * (BN / 32) / 2;
+    for (int h2 = 0; h2 < NCH; ++h2) {
       auto v = [&](int i) { const int g = h2 * NV + i; return s[qt][g / 16][g % 16]; };
-      float m = fmaxf(v(0), fmaxf(v(1), v(2)));
+      float m = fmaxf(fmaxf(v(0), v(1)), v(2));
 #pragma unroll
-      for (int i = 3; i + 1 < NV; i += 2) m = fmaxf(m, fmaxf(v(i), v(i + 1)));
-      if constexpr (NV % 2 == 0) m = fmaxf(m, v(NV - 1));
-      mx[h2] = m;
+      for (int i = 3; i + 1 < NV; i += 2) m = fmaxf(fmaxf(m, v(i)), v(i + 1));
+      mx[h2] = fmaxf(m, v(NV - 1));
     }
-    const float bmax = swap32_max(fmaxf(mx[0], mx[1]));
+    const float bmax = swap32_max(fmaxf(fmaxf(fmaxf(mx[0], mx[1]), mx[2]), mx[3]));
     const float m_new = fmaxf(m_run[qt], bmax * c_log2);
     alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
     m_run[qt] = m_new;
@@ -937,18 +939,30 @@ __device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int
   }
 }
 
-template <int D, int BN, int QT, bool CAUSAL>
+// The softmax turn. It opens with NCOPY copy instructions, group B's share of
+// the next blocks. Spreading them between the key tiles' exps (pinned there)
+// measured 4% slower.
+template <int D, int BN, int QT, bool CAUSAL, int NCOPY, typename CopyFn>
 __device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (&s)[QT][BN / 32],
                                                    bf16x8 (&pb)[QT][BN / 16],
                                                    f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
-                                                   float (&l_run)[QT]) {
+                                                   float (&l_run)[QT], CopyFn&& copy) {
+  constexpr int NB = BN / 32;
   __builtin_amdgcn_s_setprio(0);
   if (j < c.nblk && j * BN < c.kv_end_w) {
     const int kv0 = j * BN;
+#pragma unroll
+    for (int ci = 0; ci < NCOPY; ++ci) copy(ci);
     if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
-    float alpha[QT];
-    softmax_block<BN, QT>(s, pb, c.c_log2, m_run, l_run, alpha);
+    float alpha[QT], ps[QT][4];
+    softmax_stats<BN, QT>(s, c.c_log2, m_run, alpha);
+    static_for<NB>([&](auto KB) { softmax_exp<BN, QT, KB>(s, c.c_log2, m_run, ps); });
+    softmax_pack<BN, QT>(s, pb);
+    softmax_sum<QT>(l_run, alpha, ps);
     rescale_block<D, QT>(o, alpha);
+  } else {
+#pragma unroll
+    for (int ci = 0; ci < NCOPY; ++ci) copy(ci);
   }
 }
 
@@ -1012,14 +1026,14 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
       __syncthreads();
-      pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
+      pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j, s, pb, o, m_run, l_run, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 1, copy);
       }
       if (j + 1 < n) {  // block j+1 (odd): slots swap
         __syncthreads();
-        pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
+        pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j + 1, s, pb, o, m_run, l_run, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o, 1, copy);
       }
@@ -1032,17 +1046,13 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
       pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o, 0, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
-#pragma unroll
-        for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
+        pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j, s, pb, o, m_run, l_run, copy);
       }
-      pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j, s, pb, o, m_run, l_run);
       if (j + 1 < n) {
         __syncthreads();
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 0, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
-#pragma unroll
-        for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
-        pingpong_valu_turn<D, BN, QT, CAUSAL>(c, j + 1, s, pb, o, m_run, l_run);
+        pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j + 1, s, pb, o, m_run, l_run, copy);
       }
     }
     __syncthreads();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
