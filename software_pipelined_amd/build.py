@@ -31,6 +31,11 @@ def compile_cmd(out: str, extra=()) -> list:
             # device code never sees NaN (masking uses -inf, inputs are finite):
             # lets v_max_f32 / v_max3_f32 skip NaN-quieting canonicalisation
             "-Xarch_device", "-fno-honor-nans",
+            # MFMA results in VGPRs: with one wave per SIMD the compiler
+            # otherwise keeps accumulators in AGPRs and copies O back and forth
+            # every block for the VALU rescale; the Q fragments are parked in
+            # AGPRs explicitly instead
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             *extra, SRC, "-o", out]
 
 

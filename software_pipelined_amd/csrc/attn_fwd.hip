@@ -271,6 +271,19 @@ constexpr int copies_due(int step) {
   return n;
 }
 
+// With one wave per SIMD a wave has 256 VGPRs plus 256 AGPRs. The Q^T
+// fragments are only ever MFMA B operands, which may come from AGPRs, so they
+// are parked there; this keeps O (which the rescale updates on the VALU) in
+// VGPRs. Left alone, the compiler parks O in AGPRs instead and moves it out
+// and back every block (about 2 x d/2 v_accvgpr moves per block at d = 256).
+template <int QT, int ND>
+__device__ __forceinline__ void park_in_agprs(bf16x8 (&qf)[QT][ND]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kk = 0; kk < ND; ++kk) asm volatile("" : "=a"(qf[qt][kk]) : "0"(qf[qt][kk]));
+}
+
 constexpr int kPfQK = 4;  // K fragments in flight ahead of mma_qk
 constexpr int kPfPV = 2;  // V fragment pairs in flight ahead of mma_pv
 constexpr int kPfPVTurn = 3;  // the same for a ping-pong matrix turn (one wave streams alone)
@@ -672,6 +685,7 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
   // Q first, then blocks 0 .. ST-2 (so the in-loop waits count block copies only)
   bf16x8 qf[QT][D / 16];
   load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
+  if constexpr (NW * OCC <= 4) park_in_agprs<QT, D / 16>(qf);
 #pragma unroll
   for (int b = 0; b < ST - 1; ++b)
     if (b < c.nblk) {
@@ -865,6 +879,7 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipeline
   // prologue: Q; K_0, K_1 in flight; S_0 = Q K_0^T
   bf16x8 qf[QT][D / 16];
   load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
+  if constexpr (NW * OCC <= 4) park_in_agprs<QT, D / 16>(qf);
   issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
   if (c.nblk > 1)
     issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
@@ -1158,6 +1173,8 @@ const Variant kVariants[] = {
     VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_pipe", 128, 4, 64, 1, kPipelined, 2, 2),      // 20
     VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_pipe", 256, 4, 32, 1, kPipelined, 2, 1),      // 21
     VARIANT("d64_bm128_bn128_w4_q1_st2_occ2_simple", 64, 4, 128, 1, kSimple, 2, 2),       // 22
+    VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_pipe", 128, 4, 32, 2, kPipelined, 2, 1),      // 23
+    VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_simple", 128, 4, 32, 2, kSimple, 2, 1),       // 24
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
