@@ -1175,6 +1175,8 @@ const Variant kVariants[] = {
     VARIANT("d64_bm128_bn128_w4_q1_st2_occ2_simple", 64, 4, 128, 1, kSimple, 2, 2),       // 22
     VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_pipe", 128, 4, 32, 2, kPipelined, 2, 1),      // 23
     VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_simple", 128, 4, 32, 2, kSimple, 2, 1),       // 24
+    VARIANT("d64_bm256_bn64_w4_q2_st2_occ2_simple", 64, 4, 64, 2, kSimple, 2, 2),         // 25
+    VARIANT("d64_bm256_bn128_w4_q2_st2_occ1_simple", 64, 4, 128, 2, kSimple, 2, 1),       // 26
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1184,7 +1186,7 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // workgroups); 4-wave workgroups for d = 256 (O alone takes 128 registers).
 int default_variant(int d, int causal) {
   switch (d) {
-    case 64: return 22;
+    case 64: return 25;
     case 128: return 16;
     case 256: return 2;
     default: return -1;
