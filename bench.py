@@ -87,6 +87,68 @@ def cpu_baseline(cfg, q, k, v, target_s: float):
                       f"fp64 C oracle, {dt:.1f} s wall"}
 
 
+def sweep(cfg, attn, ptrs, out, lse, stream, args):
+    """Time every variant for cfg's head dim. Parity gate: a variant's output
+    must equal, bit for bit, that of the double-buffered simple schedule with
+    the same key-block size (the per-row arithmetic depends only on that)."""
+    import torch
+
+    def run(vid):
+        st = attn.attn_fwd_variant(vid, *ptrs)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    ids = [i for i in range(attn.attn_num_variants()) if attn.attn_variant_info(i)["head_dim"] == cfg.d]
+    torch.cuda.synchronize()  # inputs were uploaded on torch's stream
+    refs = {}
+    for i in ids:
+        name = attn.attn_variant_name(i)
+        bn = attn.attn_variant_info(i)["block_n"]
+        if "_st2_" in name and name.endswith("_simple") and bn not in refs:
+            run(i)
+            torch.cuda.synchronize()
+            refs[bn] = (out.clone(), lse.clone())
+            torch.cuda.synchronize()  # the clones run on torch's stream, the next kernel on ours
+    flops = cfg.flops()
+    results = []
+    for i in ids:
+        name = attn.attn_variant_name(i)
+        bn = attn.attn_variant_info(i)["block_n"]
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()  # the fill runs on torch's stream, the kernel on ours
+        run(i)
+        torch.cuda.synchronize()
+        bad_o = int((out != refs[bn][0]).sum()) if bn in refs else -1
+        bad_l = int((lse != refs[bn][1]).sum()) if bn in refs else -1
+        ok = bad_o == 0 and bad_l == 0
+        if not ok:
+            log(f"{name}: {bad_o} O and {bad_l} LSE elements differ from the reference schedule")
+            diff = (lse != refs[bn][1]).nonzero()
+            log(f"  first differing LSE (b, h, row): {diff[:6].tolist()}; "
+                f"got {lse[tuple(diff[0])].item() if diff.numel() else None}, "
+                f"reference {refs[bn][1][tuple(diff[0])].item() if diff.numel() else None}")
+        for _ in range(args.warmup):
+            run(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            run(i)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"{name:48s} {ms:8.4f} ms {tf:8.1f} TFLOP/s  parity {'ok' if ok else 'FAILED'}")
+        results.append({"variant": name, "ms": round(ms, 4), "tflops": round(tf, 1), "parity": bool(ok)})
+    good = [r for r in results if r["parity"]]
+    best = max(good, key=lambda r: r["tflops"]) if good else None
+    print(json.dumps({"sweep": cfg.name, "steps": args.steps, "warmup": args.warmup,
+                      "default": attn.attn_variant_name(attn.attn_default_variant(cfg.d, cfg.causal)),
+                      "best": best["variant"] if best else None, "results": results}), flush=True)
+    if len(good) != len(results):
+        sys.exit(1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +158,10 @@ def main():
     ap.add_argument("--variant", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every variant of the workload's head dim instead (the measured "
+                         "sweep behind the defaults); each must first reproduce, bit for bit, "
+                         "the double-buffered simple schedule of its key-block size")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -143,6 +209,10 @@ def main():
     scale = float(cfg.scale)
     ptrs = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
             cfg.B, cfg.H, cfg.N, cfg.d, int(cfg.causal), scale, stream.cuda_stream)
+
+    if args.sweep:
+        sweep(cfg, attn, ptrs, out, lse, stream, args)
+        return
 
     def step():
         st = attn.attn_fwd_variant(variant, *ptrs)

@@ -1188,7 +1188,7 @@ int default_variant(int d, int causal) {
   switch (d) {
     case 64: return 25;
     case 128: return 16;
-    case 256: return 2;
+    case 256: return 21;
     default: return -1;
   }
 }
