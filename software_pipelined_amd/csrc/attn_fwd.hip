@@ -60,7 +60,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -110,59 +109,51 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
 }
 
-// Issue the HBM -> LDS copy of BN rows (starting at row0) of one [N][D]
-// matrix. Every wave moves LOADS x 1 KiB; lane l's 16 bytes land at
-// dst + 16*l, so the swizzle is applied by choosing the source chunk. Full
-// blocks use a uniform block base plus a 32-bit per-lane offset (one VGPR per
-// copy); in the ragged last block rows past N are clamped to row N-1 (finite
-// data; those keys are masked).
+// HBM -> LDS copies of BN-row blocks of one [N][D] matrix. Every wave moves
+// LOADS x 1 KiB per block; lane l's 16 bytes land at dst + 16*l, so the
+// swizzle is applied by choosing the source chunk. The source is a buffer
+// resource over rows [row0, min(row0 + BN, N)): the hardware range check
+// turns reads of rows past N into zeros (those keys are masked and their
+// weights are exactly zero), so a copy needs no per-lane address arithmetic
+// beyond its fixed lane offset.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int D, int NW, int BN, bool IS_V>
-__device__ __forceinline__ uint32_t block_lane_offset(int t, int wave, int lane, int& row) {
+__device__ __forceinline__ uint32_t block_lane_offset(int t, int wave, int lane) {
   using T = Tile<D, NW, BN>;
   const int p = (t * NW + wave) * 64 + lane;
-  row = p / T::RC;
+  const int row = p / T::RC;
   const int pc = p % T::RC;
   const int c = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
   return (uint32_t)(row * (D * 2) + c * 16);
 }
 
-template <int D, int NW, int BN, bool IS_V>
-__device__ __forceinline__ void issue_block_load(const uint16_t* __restrict__ src, int row0, int N,
-                                                 char* dst, int wave, int lane) {
-  using T = Tile<D, NW, BN>;
-  const char* base = (const char*)src + (size_t)row0 * (D * 2);
-  if (row0 + BN <= N) {
-#pragma unroll
-    for (int t = 0; t < T::LOADS; ++t) {
-      int row;
-      const uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
-      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + off),
-                                       (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < T::LOADS; ++t) {
-      int row;
-      uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
-      const int over = row0 + row - (N - 1);
-      if (over > 0) off -= (uint32_t)(over * (D * 2));  // clamp to row N-1
-      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + off),
-                                       (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
-    }
-  }
+// row0 < N always (callers clamp block indices to the last block). The byte
+// count is made explicitly wave-uniform: a min/max clamp otherwise becomes a
+// VALU med3 and the resource a per-lane value.
+template <int D, int BN>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* src, int row0, int N) {
+  const int rows = __builtin_amdgcn_readfirstlane(min(N - row0, BN));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)row0 * D), (short)0, rows * (D * 2),
+                                           kRsrcWord3);
 }
 
-// One copy instruction (t) of a block, branch-free: rows past N-1 are
-// clamped to N-1 per lane. Used where copies are interleaved with MFMAs.
+// Copy instruction t of the block at row0.
 template <int D, int NW, int BN, bool IS_V>
 __device__ __forceinline__ void issue_copy(const uint16_t* __restrict__ src, int row0, int N, char* dst,
                                            int wave, int lane, int t) {
-  int row;
-  const uint32_t off = block_lane_offset<D, NW, BN, IS_V>(t, wave, lane, row);
-  const int over = max(row0 + row - (N - 1), 0);
-  const char* base = (const char*)src + (size_t)row0 * (D * 2);
-  __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + (off - (uint32_t)(over * (D * 2)))),
-                                   (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16), 16, 0, 0);
+  const __amdgpu_buffer_rsrc_t r = block_rsrc<D, BN>(src, row0, N);
+  const int off = (int)block_lane_offset<D, NW, BN, IS_V>(t, wave, lane);
+  LDS_AS void* to = (LDS_AS void*)(dst + (t * NW + wave) * 64 * 16);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to, 16, off, 0, 0, 0);
+}
+
+// All copy instructions of the block at row0.
+template <int D, int NW, int BN, bool IS_V>
+__device__ __forceinline__ void issue_block_load(const uint16_t* __restrict__ src, int row0, int N,
+                                                 char* dst, int wave, int lane) {
+#pragma unroll
+  for (int t = 0; t < Tile<D, NW, BN>::LOADS; ++t) issue_copy<D, NW, BN, IS_V>(src, row0, N, dst, wave, lane, t);
 }
 
 __device__ __forceinline__ float swap32_max(float x) {
