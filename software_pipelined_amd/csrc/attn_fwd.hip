@@ -23,7 +23,7 @@
 //     S accumulators into the B operand (cvt to bf16, no LDS round trip),
 //     V^T is read with the gfx950 transposing LDS read ds_read_b64_tr_b16;
 //   * K/V blocks stream through an LDS ring filled with
-//     global_load_lds_dwordx4 (HBM -> LDS without VGPRs); the destination
+//     buffer_load_dwordx4 ... lds (HBM -> LDS without VGPRs); the destination
 //     layout is XOR-swizzled per row by choosing which global chunk each lane
 //     fetches, so MFMA fragment reads are bank-conflict free;
 //   * exp2 runs on v_exp_f32 with scale*log2(e) folded into one FMA;
