@@ -445,18 +445,16 @@ __device__ __forceinline__ void softmax_block(f32x16 (&s)[QT][BN / 32], bf16x8 (
   softmax_sum<QT>(l_run, alpha, ps);
 }
 
-// rescale: O *= alpha, skipped by the whole wave when no row moved its max.
+// rescale: O *= alpha, per query tile, skipped by the whole wave when no row
+// of the tile moved its max.
 template <int D, int QT>
 __device__ __forceinline__ void rescale_block(f32x16 (&o)[QT][D / 32], const float (&alpha)[QT]) {
-  bool moved = false;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) moved = moved || (alpha[qt] != 1.0f);
-  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
+    if (__builtin_amdgcn_ballot_w64(alpha[qt] != 1.0f) != 0) {
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) o[qt][t] *= alpha[qt];
-  }
+    }
 }
 
 // mma_pv: O^T[dim][query] += V^T[dim][key] P^T[key][query]. The A operand
@@ -612,6 +610,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// makes the compiler wait for every outstanding vector-memory operation,
+// including the LDS copies of later blocks, which would cap every ring at one
+// block of copy latency. Callers wait for exactly the copies they need
+// (wait_vmcnt) before it; this wave's LDS reads have returned when it passes.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- simple kernel
 // Blocks stream through an ST-slot ring (block j in slot j mod ST): at the
 // top of block j every wave waits for its share of block j's copies, meets
@@ -630,7 +639,7 @@ __device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
   // every block issues its copies (past the last block a clamped duplicate
   // lands in a free slot), so the count of younger copies is always exact
   wait_vmcnt<(ST - 2) * PER_BLOCK>();  // blocks j+1 .. j+ST-2 may stay in flight
-  __syncthreads();
+  block_barrier();
   constexpr int NS = (SLOT + ST - 1) % ST;
   const int row_next = min(j + ST - 1, c.nblk - 1) * BN;
   const int kv0 = j * BN;
@@ -708,23 +717,25 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
 // forward schedule found by Twill, section 3.1 of the software-pipelining
 // page: the first GEMM is hoisted into the loop prologue so exp latency is
 // never exposed, and one tile's softmax overlaps the other GEMMs), restated
-// for gfx950. A wave issues at most about one VALU instruction per two VALU
-// issue slots of its SIMD, while its MFMAs run alongside its own VALU work,
-// so every phase here gives each wave both kinds of work and both waves of a
-// SIMD keep the matrix core busy together:
-//   prologue : K_0, K_1 -> LDS; S_0 = Q K_0^T
-//   block j  : (a) mma_pv(V_{j-1}, P_{j-1})  with  mask, max and exp of the
-//                  first key tile of S_j;
-//              (b) mma_qk(K_{j+1}) -> S_{j+1}  with  exp of the other key
-//                  tiles, row sum and packing of P_j;
-//              then O *= alpha_j (skipped when no row's max moved)
+// for gfx950. A wave's MFMAs run alongside its own VALU work, so every phase
+// gives the wave both kinds of work:
+//   prologue : K_0 .. K_{ST-1}, V_0 .. V_{ST-3} -> LDS; S_0 = Q K_0^T
+//   block j  : (a) mma_pv(V_{j-1}, P_{j-1})  with  mask, row max and the
+//                  first half of the exp units of S_j;
+//              (b) mma_qk(K_{j+1}) -> S_{j+1}  with  the other exp units,
+//                  row sums and packing of P_j;
+//              then O *= alpha_j per query tile (skipped for a tile when no
+//              row of it moved its max)
 //   epilogue : mma_pv(V_{n-1}, P_{n-1})
+// An exp unit is one (query tile, 32-key tile) pair, taken query-tile-major,
+// so with one key tile and two query tiles each phase gets one tile's exps.
 // O sees exactly the simple schedule's sequence of updates (... += P_{j-1}V,
-// *= alpha_j, += P_j V ...), so results agree bit for bit. LDS holds two K
-// and two V slots; at the top of block j each wave waits for K_{j+1} and
-// V_{j-1}, meets the others at the barrier (after which K_j and V_{j-2} are
-// no longer read) and, spread through phase (b), copies K_{j+2} over K_j and
-// V_j over V_{j-2}.
+// *= alpha_j, += P_j V ...), so results agree bit for bit. LDS holds ST K
+// and ST V slots (K_i and V_i in slot i mod ST). At the top of block j each
+// wave waits for its copies of K_{j+1} and V_{j-1} (those of the last ST-2
+// blocks may stay in flight), meets the others at the barrier (after which
+// K_j and V_{j-2} are no longer read) and, spread through phase (b), copies
+// K_{j+ST} over K_j and V_{j+ST-2} over V_{j-2}: ST-1 blocks of latency.
 
 // MFMA stream of NR read groups (RD reads each, feeding MR MFMAs) with NV
 // VALU instructions after every MFMA and NVM VMEM copies spread over the
@@ -754,28 +765,44 @@ __device__ __forceinline__ void sched_mfma_reads_valu_copies() {
   }
 }
 
-// Top of block j: wait for this wave's copies of K_{j+1} and V_{j-1}, meet
-// the others (K_j and V_{j-2} are then free) and return the functor that
-// copies K_{j+2} over K_j and V_j over V_{j-2} (slot SLOT of each ring); past
-// the last block a clamped duplicate lands in a slot nobody reads again.
-template <int D, int NW, int BN, int SLOT>
+template <int D, int NW, int BN, int ST, int SLOT>
 __device__ __forceinline__ auto pipe_top(const Ctx& c, char* smem, int j) {
-  wait_vmcnt<0>();
-  __syncthreads();
-  const int row_k = min(j + 2, c.nblk - 1) * BN;
-  const int row_v = j * BN;
+  constexpr int PER_BLOCK = 2 * Tile<D, NW, BN>::LOADS;  // copies per block per wave
+  wait_vmcnt<(ST - 2) * PER_BLOCK>();
+  block_barrier();
+  // past the last block a clamped duplicate lands in a slot nobody reads again
+  const int row_k = min(j + ST, c.nblk - 1) * BN;
+  const int row_v = min(j + ST - 2, c.nblk - 1) * BN;
   return [&c, smem, row_k, row_v](int ci) {
     const int t = ci >> 1;
     if (ci & 1)
-      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane, t);
+      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, ST>(smem, (SLOT + ST - 2) % ST), c.wave,
+                                  c.lane, t);
     else
-      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, 2>(smem, SLOT), c.wave, c.lane, t);
+      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, ST>(smem, SLOT), c.wave, c.lane, t);
   };
+}
+
+// Exp units [U0, U1) of S (unit u = query tile u / NB, key tile u % NB).
+template <int BN, int QT, int U0, int U1>
+__device__ __forceinline__ void softmax_exp_units(f32x16 (&s)[QT][BN / 32], float c_log2,
+                                                  const float (&m_run)[QT], float (&ps)[QT][4]) {
+  constexpr int NB = BN / 32;
+  static_for_from<U0, U1>([&](auto U) {
+    constexpr int qt = U / NB, kb = U % NB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kb][r], c_log2, -m_run[qt]));
+      s[qt][kb][r] = p;
+      if (kb == 0 && r < 4) ps[qt][r] = p;
+      else ps[qt][r & 3] += p;
+    }
+  });
 }
 
 // Block j when the whole workgroup has P_{j-1}, an unmasked S_j and a next
 // block: both phases overlapped.
-template <int D, int NW, int BN, int QT, int SLOT>
+template <int D, int NW, int BN, int QT, int ST, int SLOT>
 __device__ __forceinline__ void pipe_block_fast(const Ctx& c, char* smem, int j, const LdsOffsets<D>& off,
                                                 const bf16x8 (&qf)[QT][D / 16],
                                                 f32x16 (&s_cur)[QT][BN / 32],
@@ -784,26 +811,35 @@ __device__ __forceinline__ void pipe_block_fast(const Ctx& c, char* smem, int j,
                                                 float (&l_run)[QT]) {
   constexpr int LD = Tile<D, NW, BN>::LOADS;
   constexpr int NB = BN / 32;
-  auto copy = pipe_top<D, NW, BN, SLOT>(c, smem, j);
+  constexpr int NU = QT * NB, UA = (NU + 1) / 2;  // exp units, and those of phase (a)
+  constexpr int MA = (BN / 16) * (D / 32) * QT, MB = (D / 16) * NB * QT;  // MFMAs per phase
+  // VALU instructions placed after each MFMA: with one query tile the tuned
+  // 5 and 4; else about the phase's count (an exp unit is 16 fma, exp and
+  // add; stats take 8 max3 per key tile plus 6; packing and the sums 8 per
+  // key tile plus 4 per query tile) over its MFMAs
+  constexpr int NVA = QT == 1 ? 5 : (QT * (8 * NB + 6) + UA * 48 + MA - 1) / MA;
+  constexpr int NVB = QT == 1 ? 4 : ((NU - UA) * 48 + QT * (8 * NB + 4) + MB - 1) / MB;
+  auto copy = pipe_top<D, NW, BN, ST, SLOT>(c, smem, j);
   float alpha[QT], ps[QT][4];
-  // (a) mma_pv(V_{j-1}) with max and exp of key tile 0
-  pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT ^ 1), off, pb, o);
+  // (a) mma_pv(V_{j-1}) with the row maxima and the first exp units
+  pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, (SLOT + ST - 1) % ST), off, pb, o);
   softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
-  softmax_exp<BN, QT, 0>(s_cur, c.c_log2, m_run, ps);
+  softmax_exp_units<BN, QT, 0, UA>(s_cur, c.c_log2, m_run, ps);
+  static_for<UA>([&](auto U) {
+    pin(s_cur[U / NB][U % NB]);
+    if constexpr (U % NB == 0) {
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    pin(s_cur[qt][0]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pin(ps[qt][e]);
-  }
-  sched_mfma_reads_valu_copies<(BN / 16) * (D / 32), 2, QT, kPfPV, 5, 0>();
+      for (int e = 0; e < 4; ++e) pin(ps[U / NB][e]);
+    }
+  });
+  sched_mfma_reads_valu_copies<(BN / 16) * (D / 32), 2, QT, kPfPV, NVA, 0>();
   __builtin_amdgcn_sched_barrier(0);
-  // (b) mma_qk(K_{j+1}) with this block's copies, the remaining exps, row sum
-  // and packing. (Copies sit among the K reads: plain LDS loads whose
+  // (b) mma_qk(K_{j+1}) with this block's copies, the remaining exp units, row
+  // sums and packing. (Copies sit among the K reads: plain LDS loads whose
   // addresses the compiler can tell apart from the copy destinations; next to
   // the transposing V reads it would wait for every copy to land.)
-  qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt, copy);
-  static_for<NB - 1>([&](auto KB) { softmax_exp<BN, QT, KB + 1>(s_cur, c.c_log2, m_run, ps); });
+  qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, ST>(smem, (SLOT + 1) % ST), off, qf, s_nxt, copy);
+  softmax_exp_units<BN, QT, UA, NU>(s_cur, c.c_log2, m_run, ps);
   softmax_sum<QT>(l_run, alpha, ps);
   softmax_pack<BN, QT>(s_cur, pb);
 #pragma unroll
@@ -812,14 +848,14 @@ __device__ __forceinline__ void pipe_block_fast(const Ctx& c, char* smem, int j,
 #pragma unroll
     for (int p = 0; p < BN / 16; ++p) pin(pb[qt][p]);
   }
-  sched_mfma_reads_valu_copies<(D / 16) * NB, 1, QT, kPfQK, 4, 2 * LD>();
+  sched_mfma_reads_valu_copies<(D / 16) * NB, 1, QT, kPfQK, NVB, 2 * LD>();
   __builtin_amdgcn_sched_barrier(0);
   rescale_block<D, QT>(o, alpha);
 }
 
 // Any block (first, masked, past a wave's causal limit, last): the same
 // steps in the same order, without overlap.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int SLOT>
+template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int SLOT>
 __device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int j,
                                                    const LdsOffsets<D>& off,
                                                    const bf16x8 (&qf)[QT][D / 16],
@@ -829,7 +865,7 @@ __device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int
                                                    float (&m_run)[QT], float (&l_run)[QT]) {
   constexpr int LD = Tile<D, NW, BN>::LOADS;
   constexpr int NB = BN / 32;
-  auto copy = pipe_top<D, NW, BN, SLOT>(c, smem, j);
+  auto copy = pipe_top<D, NW, BN, ST, SLOT>(c, smem, j);
 #pragma unroll
   for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
   const int kv0 = j * BN;
@@ -838,42 +874,49 @@ __device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int
   const bool nxt = j + 1 < c.nblk && kv0 + BN < c.kv_end_w;  // S_{j+1} is needed
   float alpha[QT], ps[QT][4];
   if (prv) {
-    pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, SLOT ^ 1), off, pb, o);
+    pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, (SLOT + ST - 1) % ST), off, pb, o);
     sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
   }
   if (act) {
     if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
     softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
-    softmax_exp<BN, QT, 0>(s_cur, c.c_log2, m_run, ps);
+    softmax_exp_units<BN, QT, 0, (QT * NB + 1) / 2>(s_cur, c.c_log2, m_run, ps);
   }
   if (nxt) {
-    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, SLOT ^ 1), off, qf, s_nxt);
+    qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, (SLOT + 1) % ST), off, qf, s_nxt);
     sched_mfma_with_reads<(D / 16) * NB, 1, QT, kPfQK>();
   }
   if (act) {
-    static_for<NB - 1>([&](auto KB) { softmax_exp<BN, QT, KB + 1>(s_cur, c.c_log2, m_run, ps); });
+    softmax_exp_units<BN, QT, (QT * NB + 1) / 2, QT * NB>(s_cur, c.c_log2, m_run, ps);
     softmax_sum<QT>(l_run, alpha, ps);
     softmax_pack<BN, QT>(s_cur, pb);
     rescale_block<D, QT>(o, alpha);
   }
 }
 
-template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC>
+// NW waves, QT query tiles of 32 per wave, BN keys per block, ST ring slots
+// (even: the S buffers swap roles every block).
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int ST>
 __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipelined(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int negate_q) {
-  using T = Tile<D, NW, BN, QT, 2>;
+  static_assert(ST % 2 == 0, "the block loop is unrolled by ST and S alternates by parity");
+  using T = Tile<D, NW, BN, QT, ST>;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
   const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
 
-  // prologue: Q; K_0, K_1 in flight; S_0 = Q K_0^T
+  // prologue: Q; K_0 .. K_{ST-1} and V_0 .. V_{ST-3} in flight; S_0 = Q K_0^T
   bf16x8 qf[QT][D / 16];
   load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
   if constexpr (NW * OCC <= 4) park_in_agprs<QT, D / 16>(qf);
-  issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
-  if (c.nblk > 1)
-    issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
+  static_for<ST>([&](auto I) {
+    if (I < c.nblk) {
+      issue_block_load<D, NW, BN, false>(c.Kh, I * BN, N, k_slot<D, BN, ST>(smem, I), c.wave, c.lane);
+      if constexpr (I + 2 < ST)
+        issue_block_load<D, NW, BN, true>(c.Vh, I * BN, N, v_slot<D, BN, ST>(smem, I), c.wave, c.lane);
+    }
+  });
   const LdsOffsets<D> off(c.lane);
   f32x16 o[QT][D / 32];
   float m_run[QT], l_run[QT];
@@ -887,34 +930,47 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipeline
   f32x16 sa[QT][BN / 32], sb[QT][BN / 32];
   bf16x8 pb[QT][BN / 16];
   wait_vmcnt<0>();
-  __syncthreads();
-  qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, sa);  // block 0 is never skipped
+  block_barrier();
+  qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, 0), off, qf, sa);  // block 0 is never skipped
   sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
 
   // Blocks 1 .. jf-1 take the overlapped path for every wave: they have a
   // previous and a next block, no key past N and (causal) no key past the
   // workgroup's first query. Block 0 and blocks jf .. n-1 take the generic
-  // path. Slot and S roles alternate with the block parity.
+  // path. Block j uses slot j mod ST; S roles alternate with its parity.
   const int n = c.nblk;
   int jf = n - 1;
   if (N % BN) jf = min(jf, N / BN);
   if (CAUSAL) jf = min(jf, (c.q0 + 1) / BN);
-  pipe_block_generic<D, NW, BN, QT, CAUSAL, 0>(c, smem, 0, off, qf, sa, sb, pb, o, m_run, l_run);
+  pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, 0>(c, smem, 0, off, qf, sa, sb, pb, o, m_run, l_run);
   int j = 1;
-  for (; j + 1 < jf; j += 2) {
-    pipe_block_fast<D, NW, BN, QT, 1>(c, smem, j, off, qf, sb, sa, pb, o, m_run, l_run);
-    pipe_block_fast<D, NW, BN, QT, 0>(c, smem, j + 1, off, qf, sa, sb, pb, o, m_run, l_run);
+  for (; j + ST - 1 < jf; j += ST) {
+    static_for<ST>([&](auto I) {
+      constexpr int slot = (1 + I) % ST;
+      if constexpr ((1 + I) % 2)
+        pipe_block_fast<D, NW, BN, QT, ST, slot>(c, smem, j + I, off, qf, sb, sa, pb, o, m_run, l_run);
+      else
+        pipe_block_fast<D, NW, BN, QT, ST, slot>(c, smem, j + I, off, qf, sa, sb, pb, o, m_run, l_run);
+    });
   }
-  for (; j < n; j += 2) {
-    pipe_block_generic<D, NW, BN, QT, CAUSAL, 1>(c, smem, j, off, qf, sb, sa, pb, o, m_run, l_run);
-    if (j + 1 < n) pipe_block_generic<D, NW, BN, QT, CAUSAL, 0>(c, smem, j + 1, off, qf, sa, sb, pb, o, m_run, l_run);
+  for (; j < n; j += ST) {
+    static_for<ST>([&](auto I) {
+      constexpr int slot = (1 + I) % ST;
+      if (j + I < n) {
+        if constexpr ((1 + I) % 2)
+          pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, slot>(c, smem, j + I, off, qf, sb, sa, pb, o, m_run, l_run);
+        else
+          pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, slot>(c, smem, j + I, off, qf, sa, sb, pb, o, m_run, l_run);
+      }
+    });
   }
-  // epilogue: mma_pv of the last block (V_{n-1} copied during block n-1)
+  // epilogue: mma_pv of the last block (V_{n-1} in slot (n-1) mod ST)
   wait_vmcnt<0>();
-  __syncthreads();
+  block_barrier();
   if ((n - 1) * BN < c.kv_end_w) {
-    if ((n - 1) & 1) pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, 1), off, pb, o);
-    else pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, 0), off, pb, o);
+    static_for<ST>([&](auto I) {
+      if ((n - 1) % ST == I) pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, I), off, pb, o);
+    });
   }
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
 }
@@ -1004,7 +1060,7 @@ __device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (
 template <int D, int NW, int BN, int MS>
 __device__ __forceinline__ auto pingpong_odd_barrier(const Ctx& c, char* smem, int m) {
   wait_vmcnt<0>();
-  __syncthreads();
+  block_barrier();
   const int row_k = min(m + 2, c.nblk - 1) * BN;
   const int row_v = min(m + 1, c.nblk - 1) * BN;
   return [&c, smem, row_k, row_v](int ci) {
@@ -1045,7 +1101,7 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
   f32x16 s[QT][BN / 32];
   bf16x8 pb[QT][BN / 16];
   wait_vmcnt<0>();
-  __syncthreads();
+  block_barrier();
   const int n = c.nblk;
   constexpr int LD = Tile<D, NW, BN>::LOADS;
   auto no_copy = [](int) {};
@@ -1055,37 +1111,37 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
     sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
-      __syncthreads();
+      block_barrier();
       pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j, s, pb, o, m_run, l_run, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 1, copy);
       }
       if (j + 1 < n) {  // block j+1 (odd): slots swap
-        __syncthreads();
+        block_barrier();
         pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j + 1, s, pb, o, m_run, l_run, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o, 1, copy);
       }
     }
-    __syncthreads();  // t = 2n: group B's last mma_pv
+    block_barrier();  // t = 2n: group B's last mma_pv
   } else {
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] pv(j-1) from V slot 1, qk(j) from K slot 0 | [t=2j+1] softmax
-      __syncthreads();
+      block_barrier();
       pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o, 0, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
         pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j, s, pb, o, m_run, l_run, copy);
       }
       if (j + 1 < n) {
-        __syncthreads();
+        block_barrier();
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 0, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
         pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j + 1, s, pb, o, m_run, l_run, copy);
       }
     }
-    __syncthreads();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
+    block_barrier();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
     if (n & 1)
       pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, n - 1, off, qf, s, pb, o, 0, no_copy);
     else
@@ -1119,9 +1175,9 @@ hipError_t launch(const void* q, const void* k, const void* v, float* out, float
       hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else if constexpr (SCHED == kPipelined) {
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true, OCC, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
     else
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false, OCC, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else {
     if (causal)
       hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
@@ -1173,6 +1229,7 @@ const Variant kVariants[] = {
     VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_simple", 128, 4, 32, 2, kSimple, 2, 1),       // 24
     VARIANT("d64_bm256_bn64_w4_q2_st2_occ2_simple", 64, 4, 64, 2, kSimple, 2, 2),         // 25
     VARIANT("d64_bm256_bn128_w4_q2_st2_occ1_simple", 64, 4, 128, 2, kSimple, 2, 1),       // 26
+    VARIANT("d128_bm256_bn32_w4_q2_st4_occ1_pipe", 128, 4, 32, 2, kPipelined, 4, 1),      // 27
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
