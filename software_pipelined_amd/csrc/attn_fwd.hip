@@ -1233,15 +1233,16 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Measured choice per (head dim, mask) on MI355X: the 8-wave ping-pong
-// schedule for long non-causal d = 128; 4-wave 128-row workgroups at two or three per
-// CU where causal work is short or VALU-heavy (more, independent
-// workgroups); 4-wave workgroups for d = 256 (O alone takes 128 registers).
+// Measured choice per head dimension on MI355X (the same for both masks):
+// the 8-wave ping-pong with 128-key blocks for d = 128; for d = 64, 4-wave
+// workgroups with two query tiles per wave, two workgroups per CU; for
+// d = 256, 4-wave workgroups (O alone takes 128 registers) with the in-wave
+// pipelined schedule and 64-key blocks.
 int default_variant(int d, int causal) {
   switch (d) {
     case 64: return 25;
     case 128: return 16;
-    case 256: return 21;
+    case 256: return 18;
     default: return -1;
   }
 }
