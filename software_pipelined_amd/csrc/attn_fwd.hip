@@ -55,7 +55,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -213,24 +212,6 @@ __device__ __forceinline__ void sched_mfma_with_reads() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, MR * PF, 0);
 }
-template <int NR, int RD, int MR, int PF, int NV>
-__device__ __forceinline__ void sched_mfma_with_reads_and_valu() {
-  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
-#pragma unroll
-  for (int i = 0; i < NR - PF; ++i) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < PF * MR; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-  }
-}
 
 // Pin a value's computation before this point (an empty asm that "uses" it):
 // keeps the compiler from sinking overlapped softmax work out of the MFMA
@@ -249,7 +230,7 @@ __device__ __forceinline__ void pin(T& x) {
 // both.
 template <int NR, int PF, int NC>
 constexpr int copy_step(int c) {
-  return (c * (NR - PF)) / NC;
+  return NC > 0 ? (c * (NR - PF)) / NC : 0;
 }
 template <int NR, int PF, int NC>
 constexpr int copy_after_group(int c) {
@@ -1210,7 +1191,7 @@ const Variant kVariants[] = {
     VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_simple", 64, 4, 64, 1, kSimple, 2, 3),         // 5
     VARIANT("d256_bm128_bn32_w4_q1_st2_occ2_simple", 256, 4, 32, 1, kSimple, 2, 2),       // 6
     VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_simple", 256, 4, 32, 1, kSimple, 2, 1),       // 7
-    VARIANT("d128_bm128_bn64_w4_q1_st3_occ2_simple", 128, 4, 64, 1, kSimple, 3, 2),       // 8
+    VARIANT("d128_bm128_bn64_w4_q1_st3_occ1_simple", 128, 4, 64, 1, kSimple, 3, 1),       // 8
     VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pingpong", 128, 8, 64, 1, kPingPong, 2, 1),   // 9
     VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pipe", 128, 8, 64, 1, kPipelined, 2, 1),      // 10
     VARIANT("d64_bm256_bn64_w8_q1_st2_occ1_pipe", 64, 8, 64, 1, kPipelined, 2, 1),        // 11
