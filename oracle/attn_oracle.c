@@ -123,6 +123,48 @@ int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
   return bad;
 }
 
+/*
+ * Decoding: Nq query rows per (batch, head) against Nkv cached keys, every
+ * query seeing every key (the same definition with a rectangular score
+ * matrix, as in the split-KV decoding microbenchmark the pages list).
+ *   q : [B][H][Nq][d];  k, v : [B][H][Nkv][d]  (bf16 bits, contiguous)
+ *   rows : flat query-row ids (b*H + h)*Nq + i in [0, B*H*Nq); NULL = all
+ * Same outputs and return codes as oracle_attn_fwd_rows.
+ */
+int oracle_attn_decode_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                            int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float scale,
+                            const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                            int threads) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 1 || d < 1) return -1;
+  int64_t total = B * H * Nq;
+  if (rows == NULL) n_rows = total;
+  if (n_rows == 0) return 0;
+  if (!q || !k || !v || !out || !lse) return -1;
+  for (int64_t t = 0; rows && t < n_rows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return -1;
+  const double sigma = scale;  /* the float32 scale, widened exactly */
+  int bad = 0;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel num_threads(threads) reduction(+ : bad)
+#endif
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)Nkv);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+    for (int64_t t = 0; t < n_rows; ++t) {
+      int64_t r = rows ? rows[t] : t;
+      int64_t bh = r / Nq, i = r % Nq;
+      bad += one_row(q + bh * Nq * d, k + bh * Nkv * d, v + bh * Nkv * d, Nkv, d, 0, sigma, i, w,
+                     out + t * d, lse + t);
+    }
+    free(w);
+  }
+  (void)threads;
+  return bad;
+}
+
 /* Number of threads an OpenMP region would use by default (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -58,6 +58,13 @@ def bind(path: str):
         ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
+    lib.oracle_attn_decode_rows.restype = ctypes.c_int
+    lib.oracle_attn_decode_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -113,3 +120,41 @@ def attn_fwd(q, k, v, causal: bool, scale, threads: int = 0, lib=None):
     B, H, N, d = q.shape
     out, lse = attn_fwd_rows(q, k, v, causal, scale, None, threads, lib)
     return out.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def attn_decode_rows(q, k, v, scale, rows=None, threads: int = 0, lib=None):
+    """fp64 decoding attention: q [B, H, Nq, d] against k, v [B, H, Nkv, d],
+    every query seeing every key. ``rows``: flat query-row ids (b*H + h)*Nq + i,
+    or None for all. Returns (out [n_rows, d] float64, lse [n_rows] float64)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nkv, d] shape")
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if rows is None:
+        n_rows = B * H * Nq
+        rows_ptr = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.size
+        rows_ptr = rows.ctypes.data
+    out = np.empty((n_rows, d), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    rc = (lib or _load()).oracle_attn_decode_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nkv, d,
+        float(np.float32(scale)), rows_ptr, n_rows, out.ctypes.data, lse.ctypes.data, int(threads))
+    if rc < 0:
+        raise ValueError("oracle rejected its arguments")
+    if rc > 0:
+        raise ArithmeticError(f"{rc} softmax rows failed the sum-to-one self-check")
+    return out, lse
+
+
+def attn_decode(q, k, v, scale, threads: int = 0, lib=None):
+    """fp64 decoding attention over every query row: (out [B,H,Nq,d], lse [B,H,Nq])."""
+    B, H, Nq, d = q.shape
+    out, lse = attn_decode_rows(q, k, v, scale, None, threads, lib)
+    return out.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)

@@ -61,6 +61,41 @@ CONFIGS = [SMALL, CAUSAL_2K, LONG_16K, CAUSAL_8K_STRESS, CAUSAL_4K_D256]
 HEADLINE = LONG_16K
 
 
+@dataclass(frozen=True)
+class DecodeConfig:
+    """One decoding workload: Nq new query rows per (batch, head) against a
+    cache of Nkv keys, every query seeing every key (the split-KV decoding
+    microbenchmark of the pages' LLAMA3 configurations, (BS, SEQ) = (1, 1) and
+    (32, 1); the cache length, which the pages' table no longer shows, is taken
+    as the 4096 of their prefill configuration)."""
+
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> np.float32:
+        return default_scale(self.d)
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: both contractions over all Nq x Nkv pairs."""
+        return 4 * self.B * self.H * self.d * self.Nq * self.Nkv
+
+    def kv_bytes(self) -> int:
+        """Compulsory HBM bytes: bf16 q, k, v read once; fp32 out and lse written."""
+        return (2 * self.B * self.H * (self.Nq + 2 * self.Nkv) * self.d
+                + 4 * self.B * self.H * self.Nq * (self.d + 1))
+
+
+DECODE_B1 = DecodeConfig("decode_b1_h32_nq1_nkv4096_d128", 1, 32, 1, 4096, 128, seed=11)
+DECODE_B32 = DecodeConfig("decode_b32_h32_nq1_nkv4096_d128", 32, 32, 1, 4096, 128, seed=12)
+DECODE_CONFIGS = [DECODE_B1, DECODE_B32]
+
+
 def default_scale(d: int) -> np.float32:
     """The float32 softmax scale 1/sqrt(d) passed to both sides."""
     return np.float32(1.0 / np.sqrt(d))
@@ -98,6 +133,20 @@ def gen_qkv(B: int, H: int, N: int, d: int, seed: int, key_stress: bool = False)
 def gen_config(cfg: AttnConfig):
     """Inputs of a named workload."""
     return gen_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.key_stress)
+
+
+def gen_decode(B: int, H: int, Nq: int, Nkv: int, d: int, seed: int):
+    """Return (q [B, H, Nq, d], k [B, H, Nkv, d], v [B, H, Nkv, d]) as uint16
+    bf16 bits: Q, then K, then V drawn from one ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, H, Nq, d), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, H, Nkv, d), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, H, Nkv, d), dtype=np.float32))
+    return q, k, v
+
+
+def gen_decode_config(cfg: DecodeConfig):
+    return gen_decode(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, cfg.seed)
 
 
 def sample_rows(B: int, H: int, N: int, per_head: int, seed: int, tile: int = 64) -> np.ndarray:

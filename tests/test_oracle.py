@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import scipy.special
 
-from software_pipelined_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, gen_qkv
+from software_pipelined_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, gen_decode, gen_qkv
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
 
@@ -254,9 +254,65 @@ def check_row_subset(orc, lib=None):
         np.testing.assert_array_equal(ls, l.reshape(-1)[rows])
 
 
+# ---------------------------------------------------------------- decoding pins
+# The decoding entry point: Nq query rows against Nkv keys, every key visible.
+
+def _mp_decode(qf, kf, vf, scale):
+    """50-digit brute force of the rectangular case, independent of the oracle."""
+    import mpmath as mp
+    mp.mp.dps = 50
+    B, H, Nq, d = qf.shape
+    Nkv = kf.shape[2]
+    out = np.zeros((B, H, Nq, d))
+    lse = np.zeros((B, H, Nq))
+    sig = mp.mpf(float(np.float32(scale)))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                s = [sig * mp.fsum(mp.mpf(float(qf[b, h, i, c])) * mp.mpf(float(kf[b, h, j, c]))
+                                   for c in range(d)) for j in range(Nkv)]
+                L = mp.log(mp.fsum(mp.exp(x) for x in s))
+                lse[b, h, i] = float(L)
+                for c in range(d):
+                    out[b, h, i, c] = float(mp.fsum(mp.exp(x - L) * mp.mpf(float(vf[b, h, j, c]))
+                                                    for j, x in enumerate(s)))
+    return out, lse
+
+
+def check_decode_mpmath(orc, lib=None):
+    shapes = [(1, 1, 1, 1, 1), (1, 2, 1, 5, 4), (2, 1, 3, 2, 2), (1, 1, 2, 17, 8), (2, 2, 1, 7, 3),
+              (1, 3, 4, 9, 2)]
+    for n, (B, H, Nq, Nkv, d) in enumerate(shapes):
+        q, k, v = gen_decode(B, H, Nq, Nkv, d, seed=300 + n)
+        qf, kf, vf = (bf16_bits_to_f32(x).astype(np.float64) for x in (q, k, v))
+        scale = np.float32(1.0 / math.sqrt(d)) if n % 2 == 0 else np.float32(0.613)
+        out, lse = orc.attn_decode(q, k, v, scale, lib=lib)
+        ref_o, ref_l = _mp_decode(qf, kf, vf, scale)
+        np.testing.assert_allclose(out, ref_o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, ref_l, rtol=1e-12, atol=1e-13)
+
+
+def check_decode_uniform_and_constant(orc, lib=None):
+    # K = 0: every weight equal, O = mean of V over the whole cache, LSE = ln Nkv
+    B, H, Nq, Nkv, d = 2, 3, 2, 11, 4
+    q, k, v = gen_decode(B, H, Nq, Nkv, d, seed=7)
+    out, lse = orc.attn_decode(q, np.zeros_like(k), v, 0.5, lib=lib)
+    vf = bf16_bits_to_f32(v).astype(np.float64)
+    np.testing.assert_allclose(out, np.broadcast_to(vf.mean(axis=2, keepdims=True), out.shape),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, np.full(lse.shape, math.log(Nkv)), rtol=1e-14, atol=1e-14)
+    # V constant per (b, h): O equals that constant whatever the weights
+    cst = _bits(np.arange(B * H * d, dtype=np.float32).reshape(B, H, 1, d) * 0.25)
+    vc = np.ascontiguousarray(np.broadcast_to(cst, (B, H, Nkv, d)))
+    out, _ = orc.attn_decode(q, k, vc, 0.9, lib=lib)
+    np.testing.assert_allclose(out, np.broadcast_to(bf16_bits_to_f32(cst).astype(np.float64), out.shape),
+                               rtol=1e-13, atol=1e-13)
+
+
 ALL_CHECKS = [check_closed_forms, check_mpmath, check_library, check_constant_v, check_causal_row0,
               check_zero_keys, check_lse_bounds, check_key_shift, check_permutations,
-              check_causal_is_truncation, check_linear_in_v, check_dominant_key, check_row_subset]
+              check_causal_is_truncation, check_linear_in_v, check_dominant_key, check_row_subset,
+              check_decode_mpmath, check_decode_uniform_and_constant]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -288,13 +344,16 @@ MUTATIONS = {
                            "out_row[c] += w[j] * widen_bf16(v[c * d + (j % d)]);"),
     "log2_lse": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
     "scale_squared": ("double sigma = (double)scale;", "double sigma = (double)scale * (double)scale;"),
+    "decode_kv_head_stride": ("k + bh * Nkv * d, v + bh * Nkv * d", "k + bh * Nq * d, v + bh * Nq * d"),
+    "decode_row_split": ("int64_t bh = r / Nq, i = r % Nq;", "int64_t bh = r % (B * H), i = r / (B * H);"),
+    "decode_scale_dropped": ("const double sigma = scale;", "const double sigma = 1.0;"),
 }
 
 
 def test_planted_mistakes_are_caught(oracle_mod):
     src = open(oracle_mod.SOURCE_PATH).read()
     tmp = tempfile.mkdtemp()
-    fast_checks = [c for c in ALL_CHECKS if c is not check_mpmath]
+    fast_checks = [c for c in ALL_CHECKS if c is not check_mpmath]  # the decoding brute force is small
     try:
         for name, (old, new) in MUTATIONS.items():
             assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
