@@ -22,6 +22,8 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -36,7 +38,8 @@ enum attn_status {
   ATTN_ERR_BAD_SCALE = 4,  /* scale is NaN, infinite or zero                      */
   ATTN_ERR_MISALIGNED = 5, /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_HIP = 6,        /* the HIP runtime reported an error at launch         */
-  ATTN_ERR_BAD_VARIANT = 7 /* attn_fwd_variant: id out of range or unsuited to d */
+  ATTN_ERR_BAD_VARIANT = 7, /* attn_fwd_variant: id out of range or unsuited to d */
+  ATTN_ERR_WORKSPACE = 8    /* attn_fwd_decode: workspace smaller than required   */
 };
 
 /*
@@ -90,6 +93,41 @@ int attn_variant_info(int id, int* head_dim, int* block_m, int* block_n, int* wa
 int attn_default_variant(int d, int causal);
 int attn_fwd_variant(int id, const void* q, const void* k, const void* v, float* out, float* lse,
                      int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Split-KV decoding (PipeThreader summary page, evaluation setup: the
+ * FlashDecoding microbenchmark of the LLAMA3 models at (BS, SEQ) = (1, 1)
+ * and (32, 1); the same operation as attn_fwd with a rectangular score
+ * matrix). For every batch b and head h, Nq new query rows attend to a cache
+ * of Nkv keys, every query seeing every key:
+ *     S = scale * Q K^T  (Nq x Nkv),   O = softmax(S) V,
+ *     lse[i] = ln sum_j exp(S_ij).
+ * The keys of each (b, h) are split into chunks processed in parallel, each
+ * giving a normalised partial (O_c, LSE_c) in the workspace; a second kernel
+ * merges them: LSE = ln sum_c exp(LSE_c), O = sum_c exp(LSE_c - LSE) O_c.
+ *
+ *   q       : device, bf16, [B][H][Nq][d]
+ *   k, v    : device, bf16, [B][H][Nkv][d]
+ *   out     : device, float32, [B][H][Nq][d]; fully overwritten
+ *   lse     : device, float32, [B][H][Nq];    fully overwritten
+ *   Nq >= 0, Nkv >= 1 whenever B*H*Nq > 0; d one of 64, 128, 256
+ *   scale   : finite, nonzero float32 multiplier of q.k
+ *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
+ *             aligned, at least the size attn_decode_workspace_size reports
+ *             for the same shape (else ATTN_ERR_WORKSPACE); its contents on
+ *             entry do not matter and are overwritten
+ *   stream  : hipStream_t (NULL = default stream); two kernels are enqueued
+ *
+ * Same ownership, validation and asynchrony rules as attn_fwd; the library
+ * allocates nothing. Calls sharing one workspace must not overlap.
+ *
+ * attn_decode_workspace_size : workspace bytes for a shape (0 when
+ *             B*H*Nq == 0); same shape errors as attn_fwd_decode.
+ */
+int attn_decode_workspace_size(int B, int H, int Nq, int Nkv, int d, size_t* bytes);
+int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
+                    int Nq, int Nkv, int d, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ ATTN_ERR_BAD_SCALE = 4
 ATTN_ERR_MISALIGNED = 5
 ATTN_ERR_HIP = 6
 ATTN_ERR_BAD_VARIANT = 7
+ATTN_ERR_WORKSPACE = 8
 
 _lib = None
 
@@ -63,6 +64,11 @@ def load_library():
     lib.attn_variant_info.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int)] * 5
     lib.attn_default_variant.restype = ctypes.c_int
     lib.attn_default_variant.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.attn_decode_workspace_size.restype = ctypes.c_int
+    lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_fwd_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -105,6 +111,20 @@ def attn_default_variant(d: int, causal: bool) -> int:
     return load_library().attn_default_variant(d, int(causal))
 
 
+def attn_decode_workspace_size(B, H, Nq, Nkv, d):
+    """(status, bytes) as returned through the C ``attn_decode_workspace_size``."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_decode_workspace_size(B, H, Nq, Nkv, d, ctypes.byref(n))
+    return st, n.value
+
+
+def attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, workspace, workspace_bytes,
+                    stream) -> int:
+    """Same arguments as the C ``attn_fwd_decode``: device pointers (ints), sizes, stream."""
+    return load_library().attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, float(scale),
+                                          workspace, workspace_bytes, stream)
+
+
 # ------------------------------------------------------------ torch convenience
 
 def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, variant=None,
@@ -145,6 +165,45 @@ def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, 
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, H, N, d, causal, scale, handle)
     st = attn_fwd(*args) if variant is None else attn_fwd_variant(variant, *args)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse
+
+
+def attn_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Split-KV decoding on torch tensors already on the GPU.
+
+    q: bfloat16 [B, H, Nq, d]; k, v: bfloat16 [B, H, Nkv, d], contiguous.
+    Every query sees every key. Returns (out float32 [B, H, Nq, d], lse
+    float32 [B, H, Nq]); out, lse and the workspace (a uint8 tensor of at least
+    ``attn_decode_workspace_size`` bytes) are allocated with torch when not
+    given. Enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-d bfloat16 tensors on the GPU")
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Nkv, d) or k.shape != v.shape:
+        raise ValueError("k and v must be [B, H, Nkv, d] with q's B, H and d")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    st, need = attn_decode_workspace_size(B, H, Nq, Nkv, d)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, Nq, Nkv, d, scale, workspace.data_ptr(), workspace.numel(),
+                         stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse

@@ -64,6 +64,35 @@ def test_validation_happens_before_any_hip_call(attn):
     assert attn.attn_fwd(*good, big, big, big, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
 
 
+def test_decode_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20
+    st, need = attn.attn_decode_workspace_size(1, 32, 1, 4096, 128)
+    assert st == attn.ATTN_OK and need > 0
+    # the workspace holds one fp32 row of d + 1 values per chunk and query row
+    assert need % (4 * 129) == 0
+    assert attn.attn_decode_workspace_size(0, 32, 1, 4096, 128) == (attn.ATTN_OK, 0)
+    assert attn.attn_decode_workspace_size(1, 32, 0, 4096, 128) == (attn.ATTN_OK, 0)
+    assert attn.attn_decode_workspace_size(1, 32, 1, 4096, 96)[0] == attn.ATTN_ERR_HEAD_DIM
+    assert attn.attn_decode_workspace_size(1, -1, 1, 4096, 128)[0] == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_decode_workspace_size(1, 1, 1, 0, 128)[0] == attn.ATTN_ERR_BAD_SHAPE
+    big = 1 << 30
+    assert attn.attn_decode_workspace_size(big, big, 1, big, 128)[0] == attn.ATTN_ERR_BAD_SHAPE
+
+    def call(q=P, k=P, v=P, o=P, l=P, B=1, H=32, Nq=1, Nkv=4096, d=128, s=0.1, ws=P, wsb=None):
+        return attn.attn_fwd_decode(q, k, v, o, l, B, H, Nq, Nkv, d, s, ws, need if wsb is None else wsb,
+                                    None)
+
+    assert call(q=0) == attn.ATTN_ERR_NULL_PTR
+    assert call(ws=0) == attn.ATTN_ERR_NULL_PTR
+    assert call(d=192) == attn.ATTN_ERR_HEAD_DIM
+    assert call(Nkv=0) == attn.ATTN_ERR_BAD_SHAPE
+    assert call(s=float("nan")) == attn.ATTN_ERR_BAD_SCALE
+    assert call(k=P + 4) == attn.ATTN_ERR_MISALIGNED
+    assert call(ws=P + 8) == attn.ATTN_ERR_MISALIGNED
+    assert call(wsb=need - 1) == attn.ATTN_ERR_WORKSPACE
+    assert call(q=0, k=0, v=0, o=0, l=0, ws=0, B=0) == attn.ATTN_OK  # empty: nothing launched
+
+
 def test_variant_table(attn):
     n = attn.attn_num_variants()
     assert n >= 3
@@ -91,7 +120,7 @@ def test_variant_table(attn):
 
 
 def test_strerror_covers_every_status(attn):
-    for st in range(8):
+    for st in range(9):
         assert attn.attn_strerror(st) and attn.attn_strerror(st) != "unknown status"
     assert attn.attn_strerror(99) == "unknown status"
 
