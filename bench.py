@@ -16,6 +16,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                launch stream) against MI355X's published dense bf16 peak;
   cpu_baseline = the fp64 oracle timed on this host on a bounded row sample
                of the same workload (a reported baseline, not a target).
+
+--decode times the split-KV decoding entry (attn_fwd_decode) on a decode
+workload instead: one step = one call (partial kernel + merge kernel), and the
+rate is compulsory HBM bytes per second against MI355X's 8 TB/s.
 """
 
 from __future__ import annotations
@@ -33,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (bf16) and % of MI355X MFMA peak, N=16384 d=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "software_pipelined_amd", "csrc", "attn_fwd.hip")
 
@@ -85,6 +90,37 @@ def cpu_baseline(cfg, q, k, v, target_s: float):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} of {total_rows} query rows (seeded uniform sample, all keys per row), "
                       f"fp64 C oracle, {dt:.1f} s wall"}
+
+
+def decode_cpu_baseline(cfg, q, k, v, target_s: float):
+    """Time the fp64 oracle's decoding entry on a bounded, deterministic sample
+    of query rows; the rate is the compulsory bytes of those rows per second."""
+    import numpy as np
+    from oracle import attn_oracle
+
+    attn_oracle.build(force=False)
+    threads = attn_oracle.max_threads()
+    rng = np.random.default_rng(12345)
+    total_rows = cfg.B * cfg.H * cfg.Nq
+    calib = np.sort(rng.choice(total_rows, size=min(total_rows, 4 * threads), replace=False))
+    t0 = time.perf_counter()
+    attn_oracle.attn_decode_rows(q, k, v, cfg.scale, calib, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(total_rows, max(threads, calib.size * target_s / dt)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    # a whole decode workload can take well under target_s: repeat the sample
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        attn_oracle.attn_decode_rows(q, k, v, cfg.scale, rows, threads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    nbytes = cfg.kv_bytes() * n / total_rows * passes
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} pass(es) over {n} of {total_rows} query rows (seeded uniform sample, "
+                      f"every cached key per row), fp64 C oracle, {dt:.1f} s wall"}
 
 
 def sweep(cfg, attn, ptrs, out, lse, stream, args):
@@ -149,6 +185,74 @@ def sweep(cfg, attn, ptrs, out, lse, stream, args):
         sys.exit(1)
 
 
+def decode_bench(args):
+    """Split-KV decoding (attn_fwd_decode): HBM-bound, so the rate is compulsory
+    bytes (q, k, v read once; out, lse written) per call over the call's time."""
+    import numpy as np
+    import torch
+
+    from software_pipelined_amd import attn, inputs
+
+    cfgs = {c.name: c for c in inputs.DECODE_CONFIGS}
+    cfg = cfgs[args.workload] if args.workload else inputs.DECODE_B32
+    log(f"decode workload {cfg.name}: generating inputs")
+    q, k, v = inputs.gen_decode_config(cfg)
+    dev = torch.device("cuda:0")
+    dq, dk, dv = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device=dev)
+    st, need = attn.attn_decode_workspace_size(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d)
+    if st != 0:
+        raise attn.AttnError(st)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    args_c = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+              cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, float(cfg.scale), ws.data_ptr(), ws.numel(),
+              stream.cuda_stream)
+
+    def step():
+        st = attn.attn_fwd_decode(*args_c)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    mean_ms = float(np.mean(durs))
+    nbytes = cfg.kv_bytes()
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    log(f"{cfg.name}: call mean {mean_ms * 1e3:.1f} us, median {float(np.median(durs)) * 1e3:.1f} us; "
+        f"{gbs:.0f} GB/s of compulsory traffic ({100 * gbs / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f})")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a row sample")
+        cpu = decode_cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+    print(json.dumps({
+        "metric": "split-KV decode: compulsory HBM bytes per second (q, k, v read once; out, lse written)",
+        "value": round(nbytes * args.steps / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Nq": cfg.Nq, "Nkv": cfg.Nkv, "d": cfg.d,
+                   "bytes_per_step": nbytes, "flops_per_step": cfg.flops(), "workspace_bytes": need},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "call_us_mean": round(mean_ms * 1e3, 2),
+                     "call_us_median": round(float(np.median(durs)) * 1e3, 2),
+                     "call_us_min": round(float(min(durs)) * 1e3, 2)},
+        "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +266,9 @@ def main():
                     help="time every variant of the workload's head dim instead (the measured "
                          "sweep behind the defaults); each must first reproduce, bit for bit, "
                          "the double-buffered simple schedule of its key-block size")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the split-KV decoding entry on a decode workload instead "
+                         "(HBM-bound: reports GB/s of compulsory traffic)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -193,6 +300,10 @@ def main():
         hip_build.build_library()
     attn.load_library()
     assert torch.cuda.is_available(), "bench needs a HIP device"
+
+    if args.decode:
+        decode_bench(args)
+        return
 
     cfg = inputs.HEADLINE
     if args.workload:

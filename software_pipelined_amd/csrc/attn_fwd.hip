@@ -1249,34 +1249,76 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
                    (size_t)bh, Nq, qt0 + (lane & 31), o, m_run, l_run, lane);
 }
 
-// One wave per query row: merge the NC chunk partials of the row.
+// One workgroup per query row merges the row's NC chunk partials: the chunk
+// weights exp(LSE_c - max) are formed once in LDS, while each thread already
+// holds its first partials in registers; each thread sums one output
+// dimension over a slice of the chunks (coalesced across threads) and the
+// slices are added in LDS.
+constexpr int kDecodeMaxChunks = 2048;  // the planner never makes more
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_lse,
                                                              float* __restrict__ O, float* __restrict__ LSE,
                                                              int rows, int nc) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int G = 256 / D;  // chunk slices
+  __shared__ float w_sh[kDecodeMaxChunks];
+  __shared__ float red[256];
+  constexpr int PF = 32;      // partials per thread loaded before the weights are known
+  const int tid = threadIdx.x, row = blockIdx.x;
+  const int dim = tid % D, g = tid / D;
+  float pre[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int c = g + i * G;
+    pre[i] = c < nc ? ws_o[((size_t)c * rows + row) * D + dim] : 0.f;
+  }
   float mx = -INFINITY;
-  for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, ws_lse[(size_t)c * rows + row]);
+  for (int c = tid; c < nc; c += 256) {
+    const float l = ws_lse[(size_t)c * rows + row];
+    w_sh[c] = l;
+    mx = fmaxf(mx, l);
+  }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-  constexpr int PL = D / 64;  // dims per lane
-  float acc[PL], wsum = 0.f;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = __builtin_amdgcn_exp2f((ws_lse[(size_t)c * rows + row] - mx) * kLog2e);
-    wsum += w;
-    const float* src = ws_o + ((size_t)c * rows + row) * D;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) acc[e] += w * src[e * 64 + lane];
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float ws = 0.f;
+  for (int c = tid; c < nc; c += 256) {
+    const float w = __builtin_amdgcn_exp2f((w_sh[c] - mx) * kLog2e);  // 0 for an empty chunk
+    w_sh[c] = w;
+    ws += w;
   }
-  const float inv = 1.0f / wsum;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) O[(size_t)row * D + e * 64 + lane] = acc[e] * inv;
-  if (lane == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
+  for (int sh = 32; sh >= 1; sh >>= 1) ws += __shfl_xor(ws, sh);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = ws;
+  __syncthreads();  // also publishes every weight in w_sh
+  const float wsum = (red[4] + red[5]) + (red[6] + red[7]);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int c = g + i * G;
+    if (c < nc) acc += w_sh[c] * pre[i];
+  }
+  int c = g + PF * G;
+  for (; c + 3 * G < nc; c += 4 * G) {
+    const float* src = ws_o + ((size_t)c * rows + row) * D + dim;
+    const size_t st = (size_t)G * rows * D;
+    acc += w_sh[c] * src[0] + w_sh[c + G] * src[st] + w_sh[c + 2 * G] * src[2 * st] +
+           w_sh[c + 3 * G] * src[3 * st];
+  }
+  for (; c < nc; c += G) acc += w_sh[c] * ws_o[((size_t)c * rows + row) * D + dim];
+  __syncthreads();  // every thread has read red[4..7]
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float o = red[tid];
+#pragma unroll
+    for (int k = 1; k < G; ++k) o += red[tid + k * D];
+    O[(size_t)row * D + tid] = o / wsum;
+  }
+  if (tid == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1410,10 +1452,21 @@ int run_variant(int id, const void* q, const void* k, const void* v, float* out,
 }
 
 // Split-KV decoding: 32-key blocks, 4 waves per workgroup (2 at d = 256,
-// whose 64 KiB ring per wave fills the LDS), chunks sized so that about 2048
-// waves (8 per CU) stream the cache, a multiple of the waves per workgroup.
+// whose 64 KiB ring per wave fills the LDS). Each wave's K/V ring holds
+// 2 slots x 2 matrices x 32 keys x d bf16, so the 160 KiB LDS of a CU keeps
+// 8 waves resident at d = 64, 4 at d = 128 and 2 at d = 256; the chunks are
+// sized so that one resident round of waves (256 CUs) streams the cache,
+// rounded up to a multiple of the waves per workgroup.
 constexpr int kDecodeBN = 32;
-constexpr int kDecodeWaves = 2048;
+constexpr int kDecodeCUs = 256;
+constexpr int kDecodeLdsPerCU = 160 * 1024;
+
+constexpr int decode_waves(int d, int nw) {
+  return kDecodeCUs * (kDecodeLdsPerCU / (nw * 2 * 2 * kDecodeBN * d * 2)) * nw;
+}
+static_assert(decode_waves(64, 4) == 2048 && decode_waves(128, 4) == 1024 && decode_waves(256, 2) == 512,
+              "resident decode waves");
+static_assert(decode_waves(64, 4) <= kDecodeMaxChunks, "chunk bound of the merge");
 
 struct DecodePlan {
   int n_qt, nw, nc;
@@ -1439,11 +1492,13 @@ int decode_plan(int B, int H, int Nq, int Nkv, int d, DecodePlan* p) {
   if (rows == 0) return ATTN_OK;
   if (Nkv < 1) return ATTN_ERR_BAD_SHAPE;  // a query with no key has no softmax
   const long long groups = bh * p->n_qt;
-  if (elems_q > (1LL << 50) || elems_kv > (1LL << 50) || groups > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  if (elems_q > (1LL << 50) || elems_kv > (1LL << 50) || groups > INT_MAX || rows > INT_MAX)
+    return ATTN_ERR_BAD_SHAPE;
   const long long nblk = (Nkv + kDecodeBN - 1) / kDecodeBN;
-  long long want = (kDecodeWaves + groups - 1) / groups;
+  const long long waves = decode_waves(d, p->nw);
+  long long want = (waves + groups - 1) / groups;
   if (want > nblk) want = nblk;
-  const long long nc = ((want + p->nw - 1) / p->nw) * p->nw;
+  const long long nc = ((want + p->nw - 1) / p->nw) * p->nw;  // <= waves <= kDecodeMaxChunks
   long long floats = 0;
   if (__builtin_mul_overflow(nc * rows, (long long)(d + 1), &floats) || floats > (1LL << 40))
     return ATTN_ERR_BAD_SHAPE;
@@ -1464,7 +1519,7 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o, ws_lse, BH, Nq,
                      Nkv, p.n_qt, p.nc, c, neg);
   const int rows = (int)p.rows;
-  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)rows), dim3(256), 0, stream,
                      (const float*)ws_o, (const float*)ws_lse, out, lse, rows, p.nc);
   return hipGetLastError();
 }
