@@ -165,6 +165,158 @@ int oracle_attn_decode_rows(const uint16_t* q, const uint16_t* k, const uint16_t
   return bad;
 }
 
+/*
+ * Backward: the gradient of the forward above. The pages name the attention
+ * backward pass as a second schedule to pipeline (the Twill write-up,
+ * section 3.2) without restating it; it is the derivative of the definition
+ * above, so the oracle writes that derivative out. With dO the upstream
+ * gradient of O (the LSE output is taken to carry none) and P, O the
+ * forward's softmax and output, recomputed here in fp64:
+ *   D_i   = sum_c dO_ic O_ic
+ *   dP_ij = sum_c dO_ic v_jc                       (j in J_i)
+ *   dS_ij = P_ij (dP_ij - D_i)                     (softmax Jacobian times dP)
+ *   dQ_i  = sigma sum_{j in J_i} dS_ij k_j
+ *   dK_j  = sigma sum_{i : j in J_i} dS_ij q_i
+ *   dV_j  = sum_{i : j in J_i} P_ij dO_i
+ * For a key row, P_ij = exp(s_ij - LSE_i) with LSE_i from the row's softmax.
+ */
+
+/* Softmax row i (P into w), its output row and LSE, and D_i. */
+static int bwd_row_stats(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, int64_t N, int64_t d, int causal, double sigma,
+                         int64_t i, double* w, double* o_row, double* lse, double* D) {
+  int bad = one_row(q, k, v, N, d, causal, sigma, i, w, o_row, lse);
+  double acc = 0.0;
+  for (int64_t c = 0; c < d; ++c) acc += widen_bf16(dout[i * d + c]) * o_row[c];
+  *D = acc;
+  return bad;
+}
+
+/* dQ_i for query row i of one head. */
+static int bwd_dq_row(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* dout, int64_t N, int64_t d, int causal, double sigma,
+                      int64_t i, double* w, double* o_row, double* dq_row) {
+  double lse, D;
+  int bad = bwd_row_stats(q, k, v, dout, N, d, causal, sigma, i, w, o_row, &lse, &D);
+  int64_t nvis = causal ? i + 1 : N;
+  for (int64_t c = 0; c < d; ++c) dq_row[c] = 0.0;
+  for (int64_t j = 0; j < nvis; ++j) {
+    double dp = 0.0;
+    for (int64_t c = 0; c < d; ++c) dp += widen_bf16(dout[i * d + c]) * widen_bf16(v[j * d + c]);
+    double ds = w[j] * (dp - D);
+    for (int64_t c = 0; c < d; ++c) dq_row[c] += sigma * ds * widen_bf16(k[j * d + c]);
+  }
+  return bad;
+}
+
+/* dK_j and dV_j for key row j of one head, given every row's LSE and D. */
+static void bwd_dkdv_row(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, int64_t N, int64_t d, int causal, double sigma,
+                         const double* lse, const double* D, int64_t j, double* dk_row,
+                         double* dv_row) {
+  for (int64_t c = 0; c < d; ++c) dk_row[c] = dv_row[c] = 0.0;
+  for (int64_t i = causal ? j : 0; i < N; ++i) {
+    double dot = 0.0, dp = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      dot += widen_bf16(q[i * d + c]) * widen_bf16(k[j * d + c]);
+      dp += widen_bf16(dout[i * d + c]) * widen_bf16(v[j * d + c]);
+    }
+    double p = exp(sigma * dot - lse[i]);
+    double ds = p * (dp - D[i]);
+    for (int64_t c = 0; c < d; ++c) {
+      dv_row[c] += p * widen_bf16(dout[i * d + c]);
+      dk_row[c] += sigma * ds * widen_bf16(q[i * d + c]);
+    }
+  }
+}
+
+/*
+ * Attention backward for chosen rows.
+ *   q, k, v, dout : bf16 bits, [B][H][N][d] contiguous
+ *   qrows : flat query-row ids (b*H + h)*N + i whose dQ is wanted (NULL = all)
+ *   krows : flat key-row ids (b*H + h)*N + j whose dK, dV are wanted (NULL = all)
+ *   dq : [n_qrows][d];  dk, dv : [n_krows][d]  (doubles)
+ * Returns 0, -1 on bad arguments, or the number of softmax rows failing the
+ * sum-to-one self-check.
+ */
+int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dout, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int causal, float scale, const int64_t* qrows, int64_t n_qrows,
+                         double* dq, const int64_t* krows, int64_t n_krows, double* dk,
+                         double* dv, int threads) {
+  if (B < 0 || H < 0 || N < 0 || d < 1) return -1;
+  int64_t total = B * H * N;
+  if (qrows == NULL) n_qrows = total;
+  if (krows == NULL) n_krows = total;
+  if (!q || !k || !v || !dout) return -1;
+  if ((n_qrows > 0 && !dq) || (n_krows > 0 && (!dk || !dv))) return -1;
+  for (int64_t t = 0; qrows && t < n_qrows; ++t)
+    if (qrows[t] < 0 || qrows[t] >= total) return -1;
+  for (int64_t t = 0; krows && t < n_krows; ++t)
+    if (krows[t] < 0 || krows[t] >= total) return -1;
+  const double sigma = scale;
+  int bad = 0;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#endif
+  /* dQ rows */
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(+ : bad)
+#endif
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* o_row = (double*)malloc(sizeof(double) * (size_t)d);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+    for (int64_t t = 0; t < n_qrows; ++t) {
+      int64_t r = qrows ? qrows[t] : t;
+      int64_t head = (r / N) * N * d;
+      bad += bwd_dq_row(q + head, k + head, v + head, dout + head, N, d, causal, sigma, r % N, w,
+                        o_row, dq + t * d);
+    }
+    free(o_row);
+    free(w);
+  }
+  /* dK, dV rows, one head at a time: every row's LSE and D first */
+  double* lse = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  double* D = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  for (int64_t bh = 0; bh < B * H && n_krows > 0; ++bh) {
+    int64_t want = 0;
+    for (int64_t t = 0; t < n_krows; ++t) want += ((krows ? krows[t] : t) / N) == bh;
+    if (want == 0) continue;
+    const int64_t head = bh * N * d;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(threads) reduction(+ : bad)
+#endif
+    {
+      double* w = (double*)malloc(sizeof(double) * (size_t)N);
+      double* o_row = (double*)malloc(sizeof(double) * (size_t)d);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+      for (int64_t i = 0; i < N; ++i)
+        bad += bwd_row_stats(q + head, k + head, v + head, dout + head, N, d, causal, sigma, i, w,
+                             o_row, lse + i, D + i);
+      free(o_row);
+      free(w);
+    }
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(threads) schedule(dynamic, 4)
+#endif
+    for (int64_t t = 0; t < n_krows; ++t) {
+      int64_t r = krows ? krows[t] : t;
+      if (r / N != bh) continue;
+      bwd_dkdv_row(q + head, k + head, v + head, dout + head, N, d, causal, sigma, lse, D, r % N,
+                   dk + t * d, dv + t * d);
+    }
+  }
+  free(D);
+  free(lse);
+  (void)threads;
+  return bad;
+}
+
 /* Number of threads an OpenMP region would use by default (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

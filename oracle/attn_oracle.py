@@ -1,4 +1,5 @@
-"""Python access to the fp64 attention-forward oracle (``attn_oracle.c``).
+"""Python access to the fp64 attention oracle (``attn_oracle.c``): forward,
+decoding and backward.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path. It loads the C
@@ -63,6 +64,14 @@ def bind(path: str):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.oracle_attn_bwd_rows.restype = ctypes.c_int
+    lib.oracle_attn_bwd_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -158,3 +167,46 @@ def attn_decode(q, k, v, scale, threads: int = 0, lib=None):
     B, H, Nq, d = q.shape
     out, lse = attn_decode_rows(q, k, v, scale, None, threads, lib)
     return out.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+
+
+def attn_bwd_rows(q, k, v, dout, causal: bool, scale, qrows=None, krows=None, threads: int = 0,
+                  lib=None):
+    """fp64 attention backward (gradient of the forward) for selected rows.
+
+    q, k, v, dout: uint16 bf16 bit arrays [B, H, N, d]; dout is the upstream
+    gradient of O. ``qrows``: flat query-row ids whose dQ is wanted;
+    ``krows``: flat key-row ids whose dK and dV are wanted (None = all rows).
+    Returns (dq [n_q, d], dk [n_k, d], dv [n_k, d]) as float64.
+    """
+    arrs = [np.ascontiguousarray(x, dtype=np.uint16) for x in (q, k, v, dout)]
+    if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = arrs[0].shape
+
+    def sel(rows):
+        if rows is None:
+            return None, B * H * N, None
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        return rows, rows.size, rows.ctypes.data
+
+    qrows, n_q, qp = sel(qrows)
+    krows, n_k, kp = sel(krows)
+    dq = np.empty((n_q, d), dtype=np.float64)
+    dk = np.empty((n_k, d), dtype=np.float64)
+    dv = np.empty((n_k, d), dtype=np.float64)
+    rc = (lib or _load()).oracle_attn_bwd_rows(
+        arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data, arrs[3].ctypes.data,
+        B, H, N, d, int(bool(causal)), float(np.float32(scale)), qp, n_q, dq.ctypes.data,
+        kp, n_k, dk.ctypes.data, dv.ctypes.data, int(threads))
+    if rc < 0:
+        raise ValueError("oracle rejected its arguments")
+    if rc > 0:
+        raise ArithmeticError(f"{rc} softmax rows failed the sum-to-one self-check")
+    return dq, dk, dv
+
+
+def attn_bwd(q, k, v, dout, causal: bool, scale, threads: int = 0, lib=None):
+    """fp64 attention backward over every row: (dq, dk, dv), each [B, H, N, d]."""
+    B, H, N, d = q.shape
+    dq, dk, dv = attn_bwd_rows(q, k, v, dout, causal, scale, None, None, threads, lib)
+    return dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d)

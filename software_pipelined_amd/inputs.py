@@ -145,6 +145,21 @@ def gen_decode(B: int, H: int, Nq: int, Nkv: int, d: int, seed: int):
     return q, k, v
 
 
+def gen_dout(B: int, H: int, N: int, d: int, seed: int):
+    """Upstream gradient dO for the backward: bf16 N(0, 1) bits [B, H, N, d],
+    drawn from its own stream (entropy (seed, 0xD0)), so that Q, K, V of the
+    same seed are exactly the forward workload's."""
+    rng = np.random.default_rng((seed, 0xD0))
+    return f32_to_bf16_bits(rng.standard_normal((B, H, N, d), dtype=np.float32))
+
+
+def bwd_flops(cfg: AttnConfig) -> int:
+    """Algorithmic FLOPs of the backward: five contractions over the visible
+    pairs (S = QK^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K,
+    dK = dS^T Q), 2.5 times the forward's two."""
+    return 10 * cfg.B * cfg.H * cfg.d * cfg.visible_pairs_per_head()
+
+
 def gen_decode_config(cfg: DecodeConfig):
     return gen_decode(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, cfg.seed)
 
