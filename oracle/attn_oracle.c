@@ -198,9 +198,9 @@ static int bwd_dq_row(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       int64_t i, double* w, double* o_row, double* dq_row) {
   double lse, D;
   int bad = bwd_row_stats(q, k, v, dout, N, d, causal, sigma, i, w, o_row, &lse, &D);
-  int64_t nvis = causal ? i + 1 : N;
+  const int64_t last_key = causal ? i : N - 1;
   for (int64_t c = 0; c < d; ++c) dq_row[c] = 0.0;
-  for (int64_t j = 0; j < nvis; ++j) {
+  for (int64_t j = 0; j <= last_key; ++j) {
     double dp = 0.0;
     for (int64_t c = 0; c < d; ++c) dp += widen_bf16(dout[i * d + c]) * widen_bf16(v[j * d + c]);
     double ds = w[j] * (dp - D);
@@ -254,7 +254,7 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (qrows[t] < 0 || qrows[t] >= total) return -1;
   for (int64_t t = 0; krows && t < n_krows; ++t)
     if (krows[t] < 0 || krows[t] >= total) return -1;
-  const double sigma = scale;
+  const double sig = scale;  /* the float32 scale, widened exactly */
   int bad = 0;
 #ifdef _OPENMP
   if (threads <= 0) threads = omp_get_max_threads();
@@ -272,7 +272,7 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     for (int64_t t = 0; t < n_qrows; ++t) {
       int64_t r = qrows ? qrows[t] : t;
       int64_t head = (r / N) * N * d;
-      bad += bwd_dq_row(q + head, k + head, v + head, dout + head, N, d, causal, sigma, r % N, w,
+      bad += bwd_dq_row(q + head, k + head, v + head, dout + head, N, d, causal, sig, r % N, w,
                         o_row, dq + t * d);
     }
     free(o_row);
@@ -296,7 +296,7 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
 #pragma omp for schedule(dynamic, 4)
 #endif
       for (int64_t i = 0; i < N; ++i)
-        bad += bwd_row_stats(q + head, k + head, v + head, dout + head, N, d, causal, sigma, i, w,
+        bad += bwd_row_stats(q + head, k + head, v + head, dout + head, N, d, causal, sig, i, w,
                              o_row, lse + i, D + i);
       free(o_row);
       free(w);
@@ -307,7 +307,7 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     for (int64_t t = 0; t < n_krows; ++t) {
       int64_t r = krows ? krows[t] : t;
       if (r / N != bh) continue;
-      bwd_dkdv_row(q + head, k + head, v + head, dout + head, N, d, causal, sigma, lse, D, r % N,
+      bwd_dkdv_row(q + head, k + head, v + head, dout + head, N, d, causal, sig, lse, D, r % N,
                    dk + t * d, dv + t * d);
     }
   }
