@@ -1,6 +1,7 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) fused attention-forward library
- * (libattn.so). Plain C types only; no C++ or framework types cross it.
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention library (libattn.so):
+ * forward, split-KV decoding and backward. Plain C types only; no C++ or
+ * framework types cross it.
  *
  * The operation (PipeThreader, OSDI'25 summary page, "FlashAttention-3"
  * paragraph and Fig 7; "PipeThreader and TileLang" page, section 4.1): for
@@ -39,7 +40,7 @@ enum attn_status {
   ATTN_ERR_MISALIGNED = 5, /* a pointer is not 16-byte aligned                    */
   ATTN_ERR_HIP = 6,        /* the HIP runtime reported an error at launch         */
   ATTN_ERR_BAD_VARIANT = 7, /* attn_fwd_variant: id out of range or unsuited to d */
-  ATTN_ERR_WORKSPACE = 8    /* attn_fwd_decode: workspace smaller than required   */
+  ATTN_ERR_WORKSPACE = 8    /* decode / backward: workspace smaller than required */
 };
 
 /*
@@ -128,6 +129,40 @@ int attn_decode_workspace_size(int B, int H, int Nq, int Nkv, int d, size_t* byt
 int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
                     int Nq, int Nkv, int d, float scale, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * Attention backward (the backward pass the Twill software-pipelining
+ * write-up schedules in its section 3.2; the pages do not restate it, so it is
+ * the derivative of attn_fwd's definition). With dO the gradient of the loss
+ * with respect to out (lse is taken to carry no gradient), per (b, h):
+ *     P_ij  = exp(scale * q_i.k_j - lse_i) on visible pairs, else 0
+ *     D_i   = sum_c dO_ic out_ic,      dS_ij = P_ij (dO_i.v_j - D_i)
+ *     dv_j  = sum_i P_ij dO_i
+ *     dk_j  = scale * sum_i dS_ij q_i,  dq_i = scale * sum_j dS_ij k_j
+ *
+ *   q, k, v, dout : device, bf16, [B][H][N][d]
+ *   out, lse      : device, float32, the attn_fwd outputs for the same q, k,
+ *                   v, causal and scale ([B][H][N][d] and [B][H][N])
+ *   dq, dk, dv    : device, float32, [B][H][N][d]; fully overwritten
+ *   d             : 64 or 128 (256 returns ATTN_ERR_HEAD_DIM)
+ *   causal, scale : as for attn_fwd
+ *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
+ *                   aligned, at least attn_bwd_workspace_size bytes (else
+ *                   ATTN_ERR_WORKSPACE); its contents on entry do not matter
+ *   stream        : hipStream_t (NULL = default stream); three kernels are
+ *                   enqueued
+ *
+ * Same ownership, validation and asynchrony rules as attn_fwd; the library
+ * allocates nothing and the result is deterministic (no atomics). Calls
+ * sharing one workspace must not overlap. B*H*N == 0 returns ATTN_OK.
+ *
+ * attn_bwd_workspace_size : workspace bytes for a shape (256 bytes per 32
+ *                   query rows of each head); same shape errors as attn_bwd.
+ */
+int attn_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
+int attn_bwd(const void* q, const void* k, const void* v, const float* out, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal,
+             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

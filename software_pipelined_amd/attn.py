@@ -1,10 +1,11 @@
 """Thin Python binding of ``libattn.so`` (C ABI declared in include/attn.h).
 
-Argument marshalling only: every step of attention forward runs in the HIP
-kernels. The low-level functions take raw device pointers and sizes with the
-same names and argument order as the C entry points; ``attn_forward`` is a
-convenience wrapper that allocates ``out``/``lse`` with torch (device memory
-and streams are all torch is used for) and calls ``attn_fwd``.
+Argument marshalling only: every step of the attention forward, decoding and
+backward runs in the HIP kernels. The low-level functions take raw device
+pointers and sizes with the same names and argument order as the C entry
+points; ``attn_forward``, ``attn_decode`` and ``attn_backward`` are
+convenience wrappers that allocate outputs (and workspaces) with torch
+(device memory and streams are all torch is used for) and call them.
 
 There is no fallback: if the compiled library is missing or fails to load,
 every call raises.
@@ -66,6 +67,11 @@ def load_library():
     lib.attn_default_variant.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.attn_decode_workspace_size.restype = ctypes.c_int
     lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
     lib.attn_fwd_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -126,6 +132,61 @@ def attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, workspace, works
 
 
 # ------------------------------------------------------------ torch convenience
+
+def attn_bwd_workspace_size(B, H, N, d):
+    """(status, bytes) as returned through the C ``attn_bwd_workspace_size``."""
+    n = ctypes.c_size_t(0)
+    st = load_library().attn_bwd_workspace_size(B, H, N, d, ctypes.byref(n))
+    return st, n.value
+
+
+def attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace,
+             workspace_bytes, stream) -> int:
+    """Same arguments as the C ``attn_bwd``: device pointers (ints), sizes, stream."""
+    return load_library().attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, int(bool(causal)),
+                                   float(scale), workspace, workspace_bytes, stream)
+
+
+def attn_backward(q, k, v, out, lse, dout, causal: bool = False, scale=None, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Attention backward for torch tensors: (dq, dk, dv) float32 [B, H, N, d].
+
+    q, k, v, dout: contiguous bfloat16 [B, H, N, d] on the GPU; out (float32
+    [B, H, N, d]) and lse (float32 [B, H, N]) are the forward's outputs for
+    the same q, k, v, causal and scale. Buffers not given (and the workspace
+    of ``attn_bwd_workspace_size`` bytes) are allocated with torch.
+    """
+    import torch
+
+    for t in (q, k, v, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v, dout must be contiguous 4-d bfloat16 tensors on the GPU")
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N, d) or not out.is_contiguous():
+        raise ValueError("out must be the forward's contiguous float32 [B, H, N, d] output")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, N] output")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    st, need = attn_bwd_workspace_size(B, H, N, d)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
+                  workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return dq, dk, dv
+
 
 def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, variant=None,
                  stream=None):

@@ -93,6 +93,38 @@ def test_decode_validation_happens_before_any_hip_call(attn):
     assert call(q=0, k=0, v=0, o=0, l=0, ws=0, B=0) == attn.ATTN_OK  # empty: nothing launched
 
 
+def test_bwd_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20
+    st, need = attn.attn_bwd_workspace_size(2, 16, 1000, 128)
+    # 256 bytes of statistics per 32 query rows of each head
+    assert st == attn.ATTN_OK and need == 2 * 16 * 32 * 256
+    assert attn.attn_bwd_workspace_size(0, 16, 1000, 128) == (attn.ATTN_OK, 0)
+    assert attn.attn_bwd_workspace_size(1, 1, 1000, 256)[0] == attn.ATTN_ERR_HEAD_DIM
+    assert attn.attn_bwd_workspace_size(1, -1, 1000, 64)[0] == attn.ATTN_ERR_BAD_SHAPE
+    big = 1 << 30
+    assert attn.attn_bwd_workspace_size(big, big, big, 64)[0] == attn.ATTN_ERR_BAD_SHAPE
+
+    def call(ptrs=None, B=2, H=16, N=1000, d=128, causal=0, s=0.1, ws=P, wsb=None, **over):
+        p = dict(q=P, k=P, v=P, o=P, l=P, do=P, dq=P, dk=P, dv=P)
+        p.update(over)
+        return attn.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["l"], p["do"], p["dq"], p["dk"], p["dv"],
+                             B, H, N, d, causal, s, ws, need if wsb is None else wsb, None)
+
+    for name in ("q", "k", "v", "o", "l", "do", "dq", "dk", "dv"):
+        assert call(**{name: 0}) == attn.ATTN_ERR_NULL_PTR, name
+    assert call(ws=0) == attn.ATTN_ERR_NULL_PTR
+    assert call(d=256) == attn.ATTN_ERR_HEAD_DIM
+    assert call(N=-1) == attn.ATTN_ERR_BAD_SHAPE
+    for sc in (float("nan"), float("inf"), 0.0):
+        assert call(s=sc) == attn.ATTN_ERR_BAD_SCALE
+    assert call(do=P + 2) == attn.ATTN_ERR_MISALIGNED
+    assert call(dk=P + 8) == attn.ATTN_ERR_MISALIGNED
+    assert call(l=P + 2) == attn.ATTN_ERR_MISALIGNED
+    assert call(ws=P + 8) == attn.ATTN_ERR_MISALIGNED
+    assert call(wsb=need - 1) == attn.ATTN_ERR_WORKSPACE
+    assert call(N=0, q=0, dq=0, ws=0) == attn.ATTN_OK  # empty: nothing launched
+
+
 def test_variant_table(attn):
     n = attn.attn_num_variants()
     assert n >= 3
