@@ -17,6 +17,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline = the fp64 oracle timed on this host on a bounded row sample
                of the same workload (a reported baseline, not a target).
 
+--bwd times the attention backward (attn_bwd) on an attention workload: one
+step = one call (three kernels), rate = 10*N^2*d*B*H algorithmic flops
+(causal: visible pairs) per second against the bf16 MFMA peak.
+
 --decode times the split-KV decoding entry (attn_fwd_decode) on a decode
 workload instead: one step = one call (partial kernel + merge kernel), and the
 rate is compulsory HBM bytes per second against MI355X's 8 TB/s.
@@ -121,6 +125,108 @@ def decode_cpu_baseline(cfg, q, k, v, target_s: float):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{passes} pass(es) over {n} of {total_rows} query rows (seeded uniform sample, "
                       f"every cached key per row), fp64 C oracle, {dt:.1f} s wall"}
+
+
+def bwd_cpu_baseline(cfg, q, k, v, do, target_s: float):
+    """Time the fp64 oracle's backward on a bounded sample of query rows (dQ
+    only), credited with the 6*N*d algorithmic flops of a row's dQ (S, dP and
+    dQ rows; causal: visible keys only)."""
+    import numpy as np
+    from oracle import attn_oracle
+
+    attn_oracle.build(force=False)
+    threads = attn_oracle.max_threads()
+    rng = np.random.default_rng(12345)
+    total_rows = cfg.B * cfg.H * cfg.N
+    calib = np.sort(rng.choice(total_rows, size=min(total_rows, 4 * threads), replace=False))
+    none = np.zeros(0, dtype=np.int64)
+    t0 = time.perf_counter()
+    attn_oracle.attn_bwd_rows(q, k, v, do, cfg.causal, cfg.scale, calib, none, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(total_rows, max(threads, calib.size * target_s / dt)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    attn_oracle.attn_bwd_rows(q, k, v, do, cfg.causal, cfg.scale, rows, none, threads=threads)
+    dt = time.perf_counter() - t0
+    keys = [(int(r % cfg.N) + 1) if cfg.causal else cfg.N for r in rows]
+    flops = float(sum(6 * cfg.d * kk for kk in keys))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"dQ of {n} of {total_rows} query rows (seeded uniform sample), fp64 C oracle, "
+                      f"{dt:.1f} s wall"}
+
+
+def bwd_bench(args):
+    """Attention backward (attn_bwd: statistics, dK/dV and dQ kernels) on an
+    attention workload, with out and lse from attn_fwd and a seeded dO, all
+    resident in HBM before timing."""
+    import numpy as np
+    import torch
+
+    from software_pipelined_amd import attn, inputs
+
+    cfg = {c.name: c for c in inputs.CONFIGS}[args.workload] if args.workload else inputs.HEADLINE
+    log(f"backward workload {cfg.name}: generating inputs")
+    q, k, v = inputs.gen_config(cfg)
+    do = inputs.gen_dout(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v, do))
+    scale = float(cfg.scale)
+    out, lse = attn.attn_forward(tq, tk, tv, causal=cfg.causal, scale=scale)
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    st, need = attn.attn_bwd_workspace_size(cfg.B, cfg.H, cfg.N, cfg.d)
+    if st != 0:
+        raise attn.AttnError(st)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), tdo.data_ptr(),
+              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cfg.B, cfg.H, cfg.N, cfg.d, int(cfg.causal), scale,
+              ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def step():
+        st = attn.attn_bwd(*args_c)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    mean_ms = float(np.mean(durs))
+    flops = inputs.bwd_flops(cfg)
+    executed = flops * 14 // 10  # S and dP are formed in both main kernels
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    log(f"{cfg.name} backward: call mean {mean_ms:.3f} ms, median {float(np.median(durs)):.3f} ms; "
+        f"{achieved:.1f} TFLOP/s algorithmic ({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of "
+        f"{PEAK_BF16_TFLOPS:.0f}); MFMA work executed {executed / (mean_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a row sample")
+        cpu = bwd_cpu_baseline(cfg, q, k, v, do, args.cpu_seconds)
+    print(json.dumps({
+        "metric": "attention bwd TFLOP/s (bf16; algorithmic 2.5x the forward's flops) and % of MI355X "
+                  "MFMA peak",
+        "value": round(flops * args.steps / elapsed / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "causal": cfg.causal,
+                   "flops_per_step": flops, "mfma_flops_executed_per_step": executed,
+                   "workspace_bytes": need},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit_of_work": "one attn_bwd call (statistics, dK/dV and dQ kernels)",
+                     "call_ms_mean": round(mean_ms, 4), "call_ms_median": round(float(np.median(durs)), 4)},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def sweep(cfg, attn, ptrs, out, lse, stream, args):
@@ -269,6 +375,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time the split-KV decoding entry on a decode workload instead "
                          "(HBM-bound: reports GB/s of compulsory traffic)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the attention backward (attn_bwd) on an attention workload instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -303,6 +411,9 @@ def main():
 
     if args.decode:
         decode_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
 
     cfg = inputs.HEADLINE

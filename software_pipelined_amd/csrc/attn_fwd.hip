@@ -1346,30 +1346,35 @@ __global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __res
 constexpr int kBwdRows = 32;               // query rows per statistics block
 constexpr int kBwdStatBytes = 2 * kBwdRows * 4;  // log2e*LSE then D, fp32
 
-// Transposed-read offsets (as LdsOffsets::v) into a K-swizzled image: lane
-// rows r0 + 8r (r = 0, 1) carry different swizzles, so both are kept; adding
-// 16*p rows leaves the swizzle unchanged.
+// Compact fragment offsets into a K-swizzled [rows][D] image, one or two
+// registers per lane instead of one per fragment: the swizzle only permutes
+// 16-byte chunks within a row, so every fragment's offset is one lane base
+// XOR a compile-time constant (the row part and the chunk part occupy
+// disjoint bits).
+//   row fragment kk (A operand, ds_read_b128): row lq, chunk 2kk + h
+//       = kbase ^ (32 kk);
+//   transposed read (t, r) (ds_read_b64_tr_b16, as LdsOffsets::v): rows
+//       r0 + 8r carry different swizzles, so two bases; dims tile t
+//       = tbase[r] ^ (64 t); adding 16p rows leaves the swizzle unchanged.
 template <int D>
-struct TrOffsetsK {
-  int v[D / 32][2];
-  __device__ __forceinline__ explicit TrOffsetsK(int lane) {
-    const int h = lane >> 5, ci = lane & 15, g2 = (lane >> 4) & 1;
-    const int r0 = 4 * h + (ci >> 2);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      const int dd = t * 32 + g2 * 16 + 4 * (ci & 3);
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        v[t][r] = r0 * (D * 2) + (((dd >> 3) ^ swz_k<D>(r0 + 8 * r)) << 4) + (dd & 7) * 2;
-    }
+struct BwdOffsets {
+  int kbase, tbase0, tbase1;
+  __device__ __forceinline__ explicit BwdOffsets(int lane) {
+    const int h = lane >> 5, lq = lane & 31, ci = lane & 15, g2 = (lane >> 4) & 1;
+    kbase = lq * (D * 2) + ((h ^ swz_k<D>(lq)) << 4);
+    const int r0 = 4 * h + (ci >> 2), c1 = 2 * g2 + ((ci & 3) >> 1);
+    tbase0 = r0 * (D * 2) + ((c1 ^ swz_k<D>(r0)) << 4) + 8 * (ci & 1);
+    tbase1 = r0 * (D * 2) + ((c1 ^ swz_k<D>(r0 + 8)) << 4) + 8 * (ci & 1);
   }
+  __device__ __forceinline__ int k(int kk) const { return kbase ^ (32 * kk); }
 };
 
 // A operand of X^T[dim tile t][rows 16p .. 16p+15] from a K-swizzled image.
 template <int D>
-__device__ __forceinline__ bf16x8 read_tr_k(const char* img, const TrOffsetsK<D>& tro, int t, int p) {
-  const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + tro.v[t][0] + (p * 16) * (D * 2)));
-  const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + tro.v[t][1] + (p * 16 + 8) * (D * 2)));
+__device__ __forceinline__ bf16x8 read_tr_k(const char* img, const BwdOffsets<D>& bo, int t, int p) {
+  const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + (bo.tbase0 ^ (64 * t)) + (p * 16) * (D * 2)));
+  const i16x4 a1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + (bo.tbase1 ^ (64 * t)) + (p * 16 + 8) * (D * 2)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -1440,7 +1445,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const float* __restrict__ O
 //   P = exp2(c*S - log2e*LSE), dS = P (dP - D)   (accumulator layout: query rows)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = transposed reads, B = P / dS in bf16)
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv(
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dK,
     float* __restrict__ dV, int N, int n_ktiles, float c_log2, int negate, float scale) {
@@ -1462,8 +1467,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv(
   bf16x8 kf[1][D / 16], vf[1][D / 16];
   load_q<D, 1>(K + head, k0w, N, negate, kf, lane);  // scale < 0: S from -K, c = |scale| log2e
   load_q<D, 1>(V + head, k0w, N, 0, vf, lane);
-  const LdsOffsets<D> off(lane);
-  const TrOffsetsK<D> tro(lane);
+  const BwdOffsets<D> bo(lane);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
@@ -1491,34 +1495,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv(
     const char* Ss = Qs + 2 * MAT + wave * STAT;
     const int q0 = jb * BQ;
     if (CAUSAL && q0 + BQ - 1 < k0w) continue;  // wave-uniform: every query precedes every key of this wave
-    bf16x8 qa[D / 16], da[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      qa[kk] = *(LDS_AS const bf16x8*)(Qs + off.k[kk]);
-      da[kk] = *(LDS_AS const bf16x8*)(dOs + off.k[kk]);
-    }
+    // fragments are read right before the MFMA that consumes them: with two
+    // waves per SIMD the K/V operands and dK/dV accumulators leave little room
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[0][kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[0][kk], dp, 0, 0, 0);
-    }
-    f32x4 l2[4], dd[4];
+    for (int kk = 0; kk < D / 16; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(LDS_AS const bf16x8*)(Qs + bo.k(kk)), kf[0][kk], s, 0, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l2[g] = *(LDS_AS const f32x4*)(Ss + (8 * g + 4 * h) * 4);
-      dd[g] = *(LDS_AS const f32x4*)(Ss + BQ * 4 + (8 * g + 4 * h) * 4);
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(LDS_AS const bf16x8*)(dOs + bo.k(kk)), vf[0][kk], dp, 0, 0, 0);
     const bool diag = CAUSAL && q0 < k0w + 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2[r >> 2][r & 3]));
-      if (diag) {
-        const int qi = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        p = key > qi ? 0.f : p;
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l2 = *(LDS_AS const f32x4*)(Ss + (8 * g + 4 * h) * 4);
+      const f32x4 dd = *(LDS_AS const f32x4*)(Ss + BQ * 4 + (8 * g + 4 * h) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2[i]));
+        if (diag) {
+          const int qi = q0 + 8 * g + 4 * h + i;
+          p = key > qi ? 0.f : p;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - dd[i]);
       }
-      s[r] = p;
-      dp[r] = p * (dp[r] - dd[r >> 2][r & 3]);
     }
     bf16x8 pb[1][2], dsb[1][2];
     softmax_pack<32, 1>(*(const f32x16(*)[1][1])&s, pb);
@@ -1527,8 +1528,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv(
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        const bf16x8 ado = read_tr_k<D>(dOs, tro, t, p);
-        const bf16x8 aq = read_tr_k<D>(Qs, tro, t, p);
+        const bf16x8 ado = read_tr_k<D>(dOs, bo, t, p);
+        const bf16x8 aq = read_tr_k<D>(Qs, bo, t, p);
         dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[0][p], dv[t], 0, 0, 0);
         dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[0][p], dk[t], 0, 0, 0);
       }
@@ -1581,7 +1582,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(
   const float* st = stats + ((size_t)bh * nqb + qs / kBwdRows) * (2 * kBwdRows);
   const float l2 = st[qs % kBwdRows], dd = st[kBwdRows + qs % kBwdRows];
   const LdsOffsets<D> off(lane);
-  const TrOffsetsK<D> tro(lane);
+  const BwdOffsets<D> bo(lane);
   f32x16 dq[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dq[t] = f32x16{};
@@ -1624,7 +1625,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(
     for (int p = 0; p < BN / 16; ++p)
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
-        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr_k<D>(Ks, tro, t, p), dsb[0][p], dq[t], 0, 0, 0);
+        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr_k<D>(Ks, bo, t, p), dsb[0][p], dq[t], 0, 0, 0);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   if (qi < N) {
