@@ -1445,7 +1445,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const float* __restrict__ O
 //   P = exp2(c*S - log2e*LSE), dS = P (dP - D)   (accumulator layout: query rows)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = transposed reads, B = P / dS in bf16)
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dK,
     float* __restrict__ dV, int N, int n_ktiles, float c_log2, int negate, float scale) {
@@ -1557,7 +1557,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(
 //   dS^T = exp2(c*S^T - log2e*LSE) (dP^T - D)   (masked keys: 0)
 //   dQ^T += K^T dS^T                (A = transposed reads of the K image)
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dQ, int N,
     int n_qtiles, float c_log2, int negate, float scale) {
@@ -1842,15 +1842,21 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
   return hipGetLastError();
 }
 
-// Backward: 4 waves per workgroup in both main kernels (128 keys or 128
-// queries per workgroup), 64-key blocks in the dQ kernel, 32-row query blocks
-// in the dK/dV kernel.
-constexpr int kBwdWaves = 4;
+// Backward: two waves per SIMD in both main kernels; 64-key blocks in the dQ
+// kernel, 32-row query blocks in the dK/dV kernel; 32 keys or queries per
+// wave. The dQ kernel runs 4 waves per workgroup. The dK/dV kernel runs 8 at
+// d = 128 when that still leaves at least four workgroups per CU (each
+// workgroup streams all of Q and dO once, so wider workgroups halve that
+// traffic: -10% time at N = 16384), else 4 (more, smaller workgroups balance
+// short causal grids better); at d = 64 a 32-row block is too small to split
+// over 8 waves.
+constexpr int kBwdQWaves = 4;
+constexpr int kBwdCUs = 256;
 constexpr int kBwdBN = 64;
 
 struct BwdPlan {
   long long bh;
-  int nqb, n_tiles;
+  int nqb, kw, n_ktiles, n_qtiles;
   size_t ws_bytes;  // statistics: bh * nqb * 256 bytes
 };
 
@@ -1863,8 +1869,10 @@ int bwd_plan(int B, int H, int N, int d, BwdPlan* p) {
     return ATTN_ERR_BAD_SHAPE;
   p->bh = bh;
   p->nqb = (N + kBwdRows - 1) / kBwdRows;
-  p->n_tiles = (N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-  if (bh * p->nqb > INT_MAX || bh * p->n_tiles > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  p->kw = d == 128 && bh * ((N + 255) / 256) >= 4LL * kBwdCUs ? 8 : 4;
+  p->n_ktiles = (N + 32 * p->kw - 1) / (32 * p->kw);
+  p->n_qtiles = (N + 32 * kBwdQWaves - 1) / (32 * kBwdQWaves);
+  if (bh * p->nqb > INT_MAX) return ATTN_ERR_BAD_SHAPE;
   p->ws_bytes = (size_t)bh * p->nqb * kBwdStatBytes;
   return ATTN_OK;
 }
@@ -1878,15 +1886,21 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   // that c = |scale| log2e keeps -inf masks at -inf
   const float c = fabsf(scale) * kLog2e;
   const int neg = scale < 0.f;
-  const unsigned gp = (unsigned)(p.bh * p.nqb), gt = (unsigned)(p.bh * p.n_tiles);
+  const unsigned gp = (unsigned)(p.bh * p.nqb);
+  const unsigned gk = (unsigned)(p.bh * p.n_ktiles), gq = (unsigned)(p.bh * p.n_qtiles);
   hipLaunchKernelGGL((attn_bwd_prep<D>), dim3(gp), dim3(256), 0, stream, o, (const uint16_t*)dout, lse, stats, N,
                      p.nqb);
-  hipLaunchKernelGGL((attn_bwd_dkdv<D, kBwdWaves, CAUSAL>), dim3(gt), dim3(kBwdWaves * 64), 0, stream,
+  if (D == 128 && p.kw == 8)
+    hipLaunchKernelGGL((attn_bwd_dkdv<D, D == 128 ? 8 : 4, CAUSAL>), dim3(gk), dim3(512), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                       (const float*)stats, dk, dv, N, p.n_ktiles, c, neg, scale);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv<D, 4, CAUSAL>), dim3(gk), dim3(256), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                       (const float*)stats, dk, dv, N, p.n_ktiles, c, neg, scale);
+  hipLaunchKernelGGL((attn_bwd_dq<D, kBwdQWaves, kBwdBN, CAUSAL>), dim3(gq), dim3(kBwdQWaves * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                     (const float*)stats, dk, dv, N, p.n_tiles, c, neg, scale);
-  hipLaunchKernelGGL((attn_bwd_dq<D, kBwdWaves, kBwdBN, CAUSAL>), dim3(gt), dim3(kBwdWaves * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                     (const float*)stats, dq, N, p.n_tiles, c, neg, scale);
+                     (const float*)stats, dq, N, p.n_qtiles, c, neg, scale);
   return hipGetLastError();
 }
 

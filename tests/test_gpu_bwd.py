@@ -129,6 +129,33 @@ def test_bwd_workload_causal_2k_sampled(oracle_mod):
     compare_grads((got[0][qrows], got[1][krows], got[2][krows]), (dq, dk, dv), cfg.name)
 
 
+def _sampled_parity(oracle_mod, B, H, N, d, causal, seed, key_heads, what):
+    q, k, v = I.gen_qkv(B, H, N, d, seed=seed)
+    do = I.gen_dout(B, H, N, d, seed=seed)
+    scale = I.default_scale(d)
+    got = [x.reshape(-1, d) for x in run_bwd(q, k, v, do, causal, scale)]
+    qrows = I.sample_rows(B, H, N, per_head=4, seed=seed + 1)
+    krows = np.concatenate([h * N + I.sample_rows(1, 1, N, per_head=24, seed=seed + 2 + h) for h in key_heads])
+    dq, dk, dv = oracle_mod.attn_bwd_rows(q, k, v, do, causal, scale, qrows, krows)
+    compare_grads((got[0][qrows], got[1][krows], got[2][krows]), (dq, dk, dv), what)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_many_heads_wide_dkdv_workgroups(oracle_mod, causal):
+    """B*H*ceil(N/256) >= 1024: the dK/dV kernel runs 8-wave workgroups."""
+    _say(f"case bwd b4_h64_n1000_d128 causal={causal}")
+    _sampled_parity(oracle_mod, 4, 64, 1000, 128, causal, 41, (0, 255), f"bwd b4_h64_n1000 causal={causal}")
+
+
+def test_bwd_workload_16k_sampled(oracle_mod):
+    """The N=16384 d=128 workload at full size, as the benchmark times it:
+    dQ on sampled rows of every head, dK and dV on sampled key rows of the
+    last head."""
+    cfg = I.HEADLINE
+    _say(f"case bwd workload {cfg.name}")
+    _sampled_parity(oracle_mod, cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, cfg.seed, (cfg.B * cfg.H - 1,), cfg.name)
+
+
 def test_bwd_reuses_one_workspace(oracle_mod):
     import torch
     from software_pipelined_amd import attn
