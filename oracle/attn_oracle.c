@@ -1,5 +1,6 @@
 /*
- * Attention-forward oracle: plain, slow, fp64 CPU reference.
+ * Attention (forward, decoding, backward) and Mamba2 ChunkScan oracle: plain,
+ * slow, fp64 CPU reference.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
@@ -315,6 +316,57 @@ int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
   free(lse);
   (void)threads;
   return bad;
+}
+
+/*
+ * Mamba2 ChunkScan (PipeThreader summary page, "Running example: Mamba2" and
+ * Fig 6(a)): the sequence is processed in chunks; inside a chunk the matrix
+ * cb is scaled by the exponential decay built from dA and by dt, and its
+ * product with x is accumulated into the output. Written out, for step s of
+ * chunk c (c = s / L, m = s - cL) and head h:
+ *   out[b][s][h][:] = sum_{k = 0..m} cb[b][c][m][k]
+ *                         * exp(dA_cumsum[b][h][c][m] - dA_cumsum[b][h][c][k])
+ *                         * dt[b][h][c][k] * x[b][cL + k][h][:]
+ * Only steps k <= m of the same chunk contribute (the decay runs forward in
+ * time; the term carried across chunks by the state is a separate operation
+ * the pages do not include here).
+ *   x  : bf16 bits [B][S][H][P];   cb : bf16 bits [B][nc][L][L]
+ *   dt, dacs : float [B][H][nc][L]  (nc = ceil(S / L))
+ *   rows : flat output-row ids (b*S + s)*H + h in [0, B*S*H); NULL = all
+ *   out  : [n_rows][P] doubles
+ */
+int oracle_chunk_scan_rows(const uint16_t* x, const uint16_t* cb, const float* dt, const float* dacs,
+                           int64_t B, int64_t S, int64_t H, int64_t P, int64_t L, const int64_t* rows,
+                           int64_t n_rows, double* out, int threads) {
+  if (B < 0 || S < 0 || H < 1 || P < 1 || L < 1) return -1;
+  int64_t total = B * S * H;
+  if (rows == NULL) n_rows = total;
+  if (n_rows == 0) return 0;
+  if (!x || !cb || !dt || !dacs || !out) return -1;
+  for (int64_t t = 0; rows && t < n_rows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return -1;
+  const int64_t nc = (S + L - 1) / L;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel for num_threads(threads) schedule(dynamic, 16)
+#endif
+  for (int64_t t = 0; t < n_rows; ++t) {
+    int64_t r = rows ? rows[t] : t;
+    int64_t h = r % H, s = (r / H) % S, b = r / (H * S);
+    int64_t c = s / L, m = s % L;
+    const uint16_t* cb_row = cb + ((b * nc + c) * L + m) * L;
+    const float* dt_c = dt + ((b * H + h) * nc + c) * L;
+    const float* da_c = dacs + ((b * H + h) * nc + c) * L;
+    double* o = out + t * P;
+    for (int64_t p = 0; p < P; ++p) o[p] = 0.0;
+    for (int64_t k = 0; k <= m; ++k) {
+      double w = widen_bf16(cb_row[k]) * exp((double)da_c[m] - (double)da_c[k]) * (double)dt_c[k];
+      const uint16_t* xk = x + ((b * S + c * L + k) * H + h) * P;
+      for (int64_t p = 0; p < P; ++p) o[p] += w * widen_bf16(xk[p]);
+    }
+  }
+  (void)threads;
+  return 0;
 }
 
 /* Number of threads an OpenMP region would use by default (1 without OpenMP). */

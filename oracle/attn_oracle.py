@@ -1,5 +1,5 @@
-"""Python access to the fp64 attention oracle (``attn_oracle.c``): forward,
-decoding and backward.
+"""Python access to the fp64 oracle (``attn_oracle.c``): attention forward,
+decoding and backward, and Mamba2 ChunkScan.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path. It loads the C
@@ -73,6 +73,12 @@ def bind(path: str):
         ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.oracle_chunk_scan_rows.restype = ctypes.c_int
+    lib.oracle_chunk_scan_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -210,3 +216,38 @@ def attn_bwd(q, k, v, dout, causal: bool, scale, threads: int = 0, lib=None):
     B, H, N, d = q.shape
     dq, dk, dv = attn_bwd_rows(q, k, v, dout, causal, scale, None, None, threads, lib)
     return dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d)
+
+
+def chunk_scan_rows(x, cb, dt, dacs, L: int, rows=None, threads: int = 0, lib=None):
+    """fp64 Mamba2 ChunkScan for selected output rows.
+
+    x: uint16 bf16 bits [B, S, H, P]; cb: uint16 bf16 bits [B, nc, L, L];
+    dt, dacs: float32 [B, H, nc, L]. ``rows``: flat ids (b*S + s)*H + h, or
+    None for all. Returns out [n_rows, P] float64.
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    cb = np.ascontiguousarray(cb, dtype=np.uint16)
+    dt = np.ascontiguousarray(dt, dtype=np.float32)
+    dacs = np.ascontiguousarray(dacs, dtype=np.float32)
+    B, S, H, P = x.shape
+    nc = (S + L - 1) // L
+    if cb.shape != (B, nc, L, L) or dt.shape != (B, H, nc, L) or dacs.shape != dt.shape:
+        raise ValueError("cb must be [B, nc, L, L] and dt, dacs [B, H, nc, L]")
+    if rows is None:
+        n_rows, rows_ptr = B * S * H, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows, rows_ptr = rows.size, rows.ctypes.data
+    out = np.empty((n_rows, P), dtype=np.float64)
+    rc = (lib or _load()).oracle_chunk_scan_rows(
+        x.ctypes.data, cb.ctypes.data, dt.ctypes.data, dacs.ctypes.data, B, S, H, P, L, rows_ptr, n_rows,
+        out.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def chunk_scan(x, cb, dt, dacs, L: int, threads: int = 0, lib=None):
+    """fp64 ChunkScan over every row: out [B, S, H, P]."""
+    return chunk_scan_rows(x, cb, dt, dacs, L, None, threads, lib).reshape(x.shape)
+

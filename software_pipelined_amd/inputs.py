@@ -91,6 +91,74 @@ class DecodeConfig:
                 + 4 * self.B * self.H * self.Nq * (self.d + 1))
 
 
+@dataclass(frozen=True)
+class ChunkScanConfig:
+    """One Mamba2 ChunkScan workload: B sequences of S steps, H heads of P
+    channels, chunks of L steps (the pages' linear-attention microbenchmark
+    derived from Mamba2-1.3B, measured at BS = 64, SEQ = 8k; 64 heads of 64
+    channels and chunks of 256 are that model's published shape)."""
+
+    name: str
+    B: int
+    S: int
+    H: int
+    P: int
+    L: int
+    seed: int
+
+    @property
+    def nchunks(self) -> int:
+        return (self.S + self.L - 1) // self.L
+
+    def pairs(self) -> int:
+        """(step, earlier-or-same step) pairs inside each chunk, per (b, h)."""
+        full, tail = divmod(self.S, self.L)
+        return full * self.L * (self.L + 1) // 2 + tail * (tail + 1) // 2
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs of the contraction over the causal pairs."""
+        return 2 * self.B * self.H * self.P * self.pairs()
+
+    def hbm_bytes(self) -> int:
+        """Compulsory bytes: bf16 x and cb, fp32 dt and dA_cumsum read once,
+        fp32 out written once."""
+        return (2 * self.B * self.S * self.H * self.P + 2 * self.B * self.nchunks * self.L * self.L
+                + 2 * 4 * self.B * self.H * self.nchunks * self.L + 4 * self.B * self.S * self.H * self.P)
+
+
+def gen_chunk_scan(B: int, S: int, H: int, P: int, L: int, seed: int):
+    """Return (x, cb, dt, dA_cumsum) for ChunkScan, from ``default_rng(seed)``:
+
+      x  [B][S][H][P]          bf16 bits, N(0, 1)
+      cb [B][nc][L][L]         bf16 bits, N(0, 1) (one group: shared by all heads)
+      dt [B][H][nc][L]         fp32, uniform(0.001, 0.1) (the softplus range of
+                               Mamba2's step sizes)
+      dA_cumsum [B][H][nc][L]  fp32, the running sum within each chunk of
+                               A_h * dt with A_h = -uniform(1, 16) per head
+                               (Mamba2's A initialisation), summed in float64
+    Steps past S in the last chunk hold dt = 0 and the last running sum.
+    """
+    rng = np.random.default_rng(seed)
+    nc = (S + L - 1) // L
+    x = f32_to_bf16_bits(rng.standard_normal((B, S, H, P), dtype=np.float32))
+    cb = f32_to_bf16_bits(rng.standard_normal((B, nc, L, L), dtype=np.float32))
+    dt = rng.uniform(0.001, 0.1, size=(B, H, nc, L)).astype(np.float32)
+    valid = (np.arange(nc * L) < S).reshape(nc, L)
+    dt = np.where(valid[None, None], dt, np.float32(0.0)).astype(np.float32)
+    a = -rng.uniform(1.0, 16.0, size=(H,))
+    dacs = np.cumsum(a[None, :, None, None] * dt.astype(np.float64), axis=3).astype(np.float32)
+    return x, cb, dt, dacs
+
+
+def gen_chunk_scan_config(cfg: ChunkScanConfig):
+    return gen_chunk_scan(cfg.B, cfg.S, cfg.H, cfg.P, cfg.L, cfg.seed)
+
+
+CHUNKSCAN_SMALL = ChunkScanConfig("chunkscan_b1_s1000_h8_p64_l256", 1, 1000, 8, 64, 256, seed=21)
+CHUNKSCAN_B64 = ChunkScanConfig("chunkscan_b64_s8192_h64_p64_l256", 64, 8192, 64, 64, 256, seed=22)
+CHUNKSCAN_CONFIGS = [CHUNKSCAN_SMALL, CHUNKSCAN_B64]
+
+
 DECODE_B1 = DecodeConfig("decode_b1_h32_nq1_nkv4096_d128", 1, 32, 1, 4096, 128, seed=11)
 DECODE_B32 = DecodeConfig("decode_b32_h32_nq1_nkv4096_d128", 32, 32, 1, 4096, 128, seed=12)
 DECODE_CONFIGS = [DECODE_B1, DECODE_B32]
