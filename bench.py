@@ -21,6 +21,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
 step = one call (three kernels), rate = 10*N^2*d*B*H algorithmic flops
 (causal: visible pairs) per second against the bf16 MFMA peak.
 
+--chunkscan times the Mamba2 ChunkScan entry (chunk_scan) on a ChunkScan
+workload: one step = one call, rate = compulsory HBM bytes per second.
+
 --decode times the split-KV decoding entry (attn_fwd_decode) on a decode
 workload instead: one step = one call (partial kernel + merge kernel), and the
 rate is compulsory HBM bytes per second against MI355X's 8 TB/s.
@@ -229,6 +232,92 @@ def bwd_bench(args):
         "cpu_baseline": cpu}), flush=True)
 
 
+def chunkscan_cpu_baseline(cfg, x, cb, dt, dacs, target_s: float):
+    """Time the fp64 oracle's ChunkScan on a bounded, deterministic row sample;
+    the rate is the compulsory bytes of those rows per second."""
+    import numpy as np
+    from oracle import attn_oracle
+
+    attn_oracle.build(force=False)
+    threads = attn_oracle.max_threads()
+    rng = np.random.default_rng(12345)
+    total_rows = cfg.B * cfg.S * cfg.H
+    calib = np.sort(rng.choice(total_rows, size=min(total_rows, 64 * threads), replace=False))
+    t0 = time.perf_counter()
+    attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, calib, threads=threads)
+    dt_s = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(total_rows, max(threads, calib.size * target_s / dt_s)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows, threads=threads)
+    dt_s = time.perf_counter() - t0
+    nbytes = cfg.hbm_bytes() * n / total_rows
+    return {"value": nbytes / dt_s / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {total_rows} output rows (seeded uniform sample), fp64 C oracle, {dt_s:.1f} s wall"}
+
+
+def chunkscan_bench(args):
+    """Mamba2 ChunkScan (chunk_scan): HBM-bound, so the rate is compulsory
+    bytes (x, cb, dt, dA_cumsum read once; out written once) per call time."""
+    import numpy as np
+    import torch
+
+    from software_pipelined_amd import attn, inputs
+
+    cfgs = {c.name: c for c in inputs.CHUNKSCAN_CONFIGS}
+    cfg = cfgs[args.workload] if args.workload else inputs.CHUNKSCAN_B64
+    log(f"chunk scan workload {cfg.name}: generating inputs")
+    x, cb, dt, dacs = inputs.gen_chunk_scan_config(cfg)
+    dev = torch.device("cuda:0")
+    tx, tcb = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev) for a in (x, cb))
+    tdt, tda = torch.from_numpy(dt).to(dev), torch.from_numpy(dacs).to(dev)
+    out = torch.empty((cfg.B, cfg.S, cfg.H, cfg.P), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    args_c = (tx.data_ptr(), tcb.data_ptr(), tdt.data_ptr(), tda.data_ptr(), out.data_ptr(), cfg.B, cfg.S, cfg.H,
+              cfg.P, cfg.L, stream.cuda_stream)
+
+    def step():
+        st = attn.chunk_scan(*args_c)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    mean_ms = float(np.mean(durs))
+    nbytes = cfg.hbm_bytes()
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    log(f"{cfg.name}: call mean {mean_ms:.3f} ms, median {float(np.median(durs)):.3f} ms; {gbs:.0f} GB/s of "
+        f"compulsory traffic ({100 * gbs / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}); "
+        f"{cfg.flops() / (mean_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a row sample")
+        cpu = chunkscan_cpu_baseline(cfg, x, cb, dt, dacs, args.cpu_seconds)
+    print(json.dumps({
+        "metric": "Mamba2 ChunkScan: compulsory HBM bytes per second (x, cb, dt, dA_cumsum read once; out written)",
+        "value": round(nbytes * args.steps / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "S": cfg.S, "H": cfg.H, "P": cfg.P, "L": cfg.L,
+                   "bytes_per_step": nbytes, "flops_per_step": cfg.flops()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "call_ms_mean": round(mean_ms, 4), "call_ms_median": round(float(np.median(durs)), 4)},
+        "cpu_baseline": cpu}), flush=True)
+
+
 def sweep(cfg, attn, ptrs, out, lse, stream, args):
     """Time every variant for cfg's head dim. Parity gate: a variant's output
     must equal, bit for bit, that of the double-buffered simple schedule with
@@ -377,6 +466,9 @@ def main():
                          "(HBM-bound: reports GB/s of compulsory traffic)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the attention backward (attn_bwd) on an attention workload instead")
+    ap.add_argument("--chunkscan", action="store_true",
+                    help="time the Mamba2 ChunkScan entry (chunk_scan) on a ChunkScan workload instead "
+                         "(HBM-bound: reports GB/s of compulsory traffic)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -414,6 +506,9 @@ def main():
         return
     if args.bwd:
         bwd_bench(args)
+        return
+    if args.chunkscan:
+        chunkscan_bench(args)
         return
 
     cfg = inputs.HEADLINE

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused attention library (libattn.so):
- * forward, split-KV decoding and backward. Plain C types only; no C++ or
- * framework types cross it.
+ * forward, split-KV decoding and backward, and Mamba2 ChunkScan. Plain C
+ * types only; no C++ or framework types cross it.
  *
  * The operation (PipeThreader, OSDI'25 summary page, "FlashAttention-3"
  * paragraph and Fig 7; "PipeThreader and TileLang" page, section 4.1): for
@@ -163,6 +163,33 @@ int attn_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 int attn_bwd(const void* q, const void* k, const void* v, const float* out, const float* lse,
              const void* dout, float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal,
              float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mamba2 ChunkScan (PipeThreader summary page, "Running example: Mamba2" and
+ * Fig 6(a); the linear-attention microbenchmark derived from Mamba2-1.3B).
+ * The sequence is cut into chunks of L steps; inside a chunk, cb is scaled
+ * by the exponential decay built from dA and by dt, and its product with x
+ * accumulates into the output. For step s (chunk c = s / L, m = s - cL):
+ *     out[b][s][h][:] = sum_{k=0..m} cb[b][c][m][k]
+ *                        * exp(dA_cumsum[b][h][c][m] - dA_cumsum[b][h][c][k])
+ *                        * dt[b][h][c][k] * x[b][cL + k][h][:]
+ * (only earlier-or-same steps of the same chunk; the contribution carried
+ * across chunks by the state is a separate operation).
+ *
+ *   x          : device, bf16, [B][S][H][P]
+ *   cb         : device, bf16, [B][nc][L][L]  (nc = ceil(S / L); one group,
+ *                shared by all heads)
+ *   dt, dA_cumsum : device, float32, [B][H][nc][L] (dA_cumsum: the running
+ *                sum of dA within each chunk)
+ *   out        : device, float32, [B][S][H][P]; fully overwritten
+ *   P          : 64 (else ATTN_ERR_HEAD_DIM); L a multiple of 32 in [32, 256]
+ *   stream     : hipStream_t (NULL = default stream)
+ *
+ * Same ownership, validation and asynchrony rules as attn_fwd (all five
+ * pointers 16-byte aligned). B*S == 0 returns ATTN_OK and launches nothing.
+ */
+int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_cumsum, float* out, int B, int S,
+               int H, int P, int L, void* stream);
 
 #ifdef __cplusplus
 }

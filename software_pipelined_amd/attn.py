@@ -1,9 +1,10 @@
 """Thin Python binding of ``libattn.so`` (C ABI declared in include/attn.h).
 
 Argument marshalling only: every step of the attention forward, decoding and
-backward runs in the HIP kernels. The low-level functions take raw device
+backward and of the Mamba2 ChunkScan runs in the HIP kernels. The low-level functions take raw device
 pointers and sizes with the same names and argument order as the C entry
-points; ``attn_forward``, ``attn_decode`` and ``attn_backward`` are
+points; ``attn_forward``, ``attn_decode``, ``attn_backward`` and
+``mamba_chunk_scan`` are
 convenience wrappers that allocate outputs (and workspaces) with torch
 (device memory and streams are all torch is used for) and call them.
 
@@ -72,6 +73,8 @@ def load_library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.chunk_scan.restype = ctypes.c_int
+    lib.chunk_scan.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
     lib.attn_fwd_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -186,6 +189,41 @@ def attn_backward(q, k, v, out, lse, dout, causal: bool = False, scale=None, dq=
     if st != ATTN_OK:
         raise AttnError(st)
     return dq, dk, dv
+
+
+def chunk_scan(x, cb, dt, dA_cumsum, out, B, S, H, P, L, stream) -> int:
+    """Same arguments as the C ``chunk_scan``: device pointers (ints), sizes, stream."""
+    return load_library().chunk_scan(x, cb, dt, dA_cumsum, out, B, S, H, P, L, stream)
+
+
+def mamba_chunk_scan(x, cb, dt, dA_cumsum, L: int, out=None, stream=None):
+    """Mamba2 ChunkScan for torch tensors: out float32 [B, S, H, P].
+
+    x: bfloat16 [B, S, H, P]; cb: bfloat16 [B, nc, L, L]; dt, dA_cumsum:
+    float32 [B, H, nc, L] (nc = ceil(S / L)); all contiguous on the GPU.
+    """
+    import torch
+
+    if x.dtype != torch.bfloat16 or cb.dtype != torch.bfloat16 or x.dim() != 4:
+        raise ValueError("x and cb must be bfloat16, x [B, S, H, P]")
+    B, S, H, P = x.shape
+    nc = (S + L - 1) // L
+    if tuple(cb.shape) != (B, nc, L, L) or tuple(dt.shape) != (B, H, nc, L) or dt.shape != dA_cumsum.shape:
+        raise ValueError("cb must be [B, nc, L, L] and dt, dA_cumsum [B, H, nc, L]")
+    for t in (x, cb, dt, dA_cumsum):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous GPU tensors")
+    if dt.dtype != torch.float32 or dA_cumsum.dtype != torch.float32:
+        raise ValueError("dt and dA_cumsum must be float32")
+    if out is None:
+        out = torch.empty((B, S, H, P), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = chunk_scan(x.data_ptr(), cb.data_ptr(), dt.data_ptr(), dA_cumsum.data_ptr(), out.data_ptr(),
+                    B, S, H, P, L, stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out
 
 
 def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, variant=None,

@@ -1639,6 +1639,127 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
   }
 }
 
+// ---------------------------------------------------------------- Mamba2 ChunkScan
+// PipeThreader summary page, "Running example: Mamba2" and Fig 6(a): inside
+// each chunk of L steps, cb is scaled by the exponential decay built from dA
+// and by dt, and its product with x accumulates into the output:
+//   out[b][s][h][:] = sum_{k <= m} cb[b][c][m][k] exp(dAc[m] - dAc[k]) dt[k] x[b][cL+k][h][:]
+// (m = s - cL, dAc = the running sum of dA within the chunk). The same MFMA
+// mapping as the forward's mma_pv: out^T[p][m] += x^T[p][k] A^T[k][m] with
+// A[m][k] = cb[m][k] exp(dAc[m] - dAc[k]) dt[k] formed in registers straight
+// into the B-operand layout (so A never exists in memory) and x^T read from
+// an LDS image of the 32-step block with the transposing LDS read. One
+// workgroup per (b, chunk, h): 4 waves, wave w owns chunk rows 64w .. 64w+63;
+// the 32-step x blocks stream through a two-slot ring. Workgroup ids run
+// over heads fastest, so the heads sharing one cb chunk run together.
+constexpr int kCsP = 64;   // channels per head
+constexpr int kCsBK = 32;  // steps per x block
+
+// Copy of x rows [row0, row0 + 32) of one (b, h) (row stride H*P) into an
+// LDS image in V layout: one 1 KiB instruction per wave; rows past the chunk
+// end read zeros.
+__device__ __forceinline__ void cs_copy_x(const uint16_t* xh, int row0, int rows_valid, int row_stride, char* dst,
+                                          int wave, int lane) {
+  const int pidx = wave * 64 + lane;
+  const int row = pidx >> 3, pc = pidx & 7;
+  const int c = pc ^ swz_v<kCsP>(row);
+  const int bytes = __builtin_amdgcn_readfirstlane((rows_valid - 1) * row_stride * 2 + kCsP * 2);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(xh + (size_t)row0 * row_stride), (short)0, bytes, kRsrcWord3);
+  LDS_AS void* to = (LDS_AS void*)(dst + wave * 64 * 16);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to, 16, row * row_stride * 2 + c * 16, 0, 0, 0);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __restrict__ X, const uint16_t* __restrict__ CB,
+                                                         const float* __restrict__ DT, const float* __restrict__ DAC,
+                                                         float* __restrict__ OUT, int S, int H, int L, int nc) {
+  static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block");
+  constexpr int XB = kCsBK * kCsP * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * XB];
+  const int lane = threadIdx.x & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x % H, c = (blockIdx.x / H) % nc, b = blockIdx.x / (H * nc);
+  const int c0 = c * L, Lc = min(L, S - c0);
+  const int nblk = (Lc + kCsBK - 1) / kCsBK;
+  const int row_stride = H * kCsP;
+  const uint16_t* xh = X + ((size_t)b * S + c0) * row_stride + (size_t)h * kCsP;
+  const uint16_t* cbc = CB + ((size_t)b * nc + c) * L * L;
+  const size_t sc = (((size_t)b * H + h) * nc + c) * L;
+  const float* dtc = DT + sc;
+  const float* dac = DAC + sc;
+  const int mw = 64 * wave;  // first chunk row of this wave
+
+  float dam[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) dam[qt] = dac[min(mw + 32 * qt + (lane & 31), Lc - 1)];
+  const LdsOffsets<kCsP> off(lane);
+  f32x16 o[2][kCsP / 32];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < kCsP / 32; ++t) o[qt][t] = f32x16{};
+
+  cs_copy_x(xh, 0, min(kCsBK, Lc), row_stride, smem, wave, lane);
+  for (int j = 0; j < nblk; ++j) {
+    wait_vmcnt<0>();
+    block_barrier();
+    if (j + 1 < nblk)
+      cs_copy_x(xh, (j + 1) * kCsBK, min(kCsBK, Lc - (j + 1) * kCsBK), row_stride, smem + ((j + 1) & 1) * XB, wave,
+                lane);
+    const int k0 = j * kCsBK;
+    if (mw >= Lc || k0 > mw + 63) continue;  // wave-uniform: no row of this wave sees the block
+    // dt and dA_cumsum of this lane's 16 steps: k0 + 16hf + 8e + 4hl + i
+    f32x4 dtv[2][2], dav[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        dtv[hf][e] = *(const f32x4*)(dtc + k0 + 16 * hf + 8 * e + 4 * hl);
+        dav[hf][e] = *(const f32x4*)(dac + k0 + 16 * hf + 8 * e + 4 * hl);
+      }
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int m = mw + 32 * qt + (lane & 31);
+      const uint16_t* cbr = cbc + (size_t)min(m, L - 1) * L + k0 + 4 * hl;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint2 raw = *(const uint2*)(cbr + 16 * hf + 8 * e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = i < 2 ? raw.x : raw.y;
+            const float cbv = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            const int kk = k0 + 16 * hf + 8 * e + 4 * hl + i;
+            const float decay = __builtin_amdgcn_exp2f((dam[qt] - dav[hf][e][i]) * kLog2e);
+            a[4 * e + i] = kk <= m ? cbv * decay * dtv[hf][e][i] : 0.f;
+          }
+        }
+        pb[qt][hf] = bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                            (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
+      }
+    }
+    pv_block<kCsP, kCsBK, 2>(smem + (j & 1) * XB, off, pb, o);
+  }
+  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int m = mw + 32 * qt + (lane & 31);
+    if (m < Lc) {
+      float* orow = OUT + (((size_t)b * S + c0 + m) * H + h) * kCsP;
+#pragma unroll
+      for (int t = 0; t < kCsP / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(orow + t * 32 + g * 8 + hl * 4) =
+              f32x4{o[qt][t][4 * g], o[qt][t][4 * g + 1], o[qt][t][4 * g + 2], o[qt][t][4 * g + 3]};
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 typedef hipError_t (*launch_fn)(const void*, const void*, const void*, float*, float*, int, int,
@@ -1904,6 +2025,22 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   return hipGetLastError();
 }
 
+// ChunkScan: P = 64 channels per head; chunk length a multiple of 32, at most
+// 256 (four waves of 64 rows).
+int chunk_scan_check(int B, int S, int H, int P, int L, long long* groups) {
+  if (B < 0 || S < 0 || H < 1) return ATTN_ERR_BAD_SHAPE;
+  if (P != kCsP) return ATTN_ERR_HEAD_DIM;
+  if (L < kCsBK || L > 256 || L % kCsBK != 0) return ATTN_ERR_BAD_SHAPE;
+  long long rows = 0, elems = 0, g = 0;
+  const long long nc = ((long long)S + L - 1) / L;
+  if (__builtin_mul_overflow((long long)B * S, (long long)H, &rows) || __builtin_mul_overflow(rows, (long long)P, &elems) ||
+      elems > (1LL << 50) || __builtin_mul_overflow((long long)B * nc, (long long)H, &g) || g > INT_MAX ||
+      (long long)H * P * 2 * kCsBK > INT_MAX)
+    return ATTN_ERR_BAD_SHAPE;
+  *groups = g;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2021,6 +2158,21 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* out, cons
     e = causal ? launch_bwd<128, true>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm)
                : launch_bwd<128, false>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_cumsum, float* out, int B, int S,
+               int H, int P, int L, void* stream) {
+  long long groups = 0;
+  const int st = chunk_scan_check(B, S, H, P, L, &groups);
+  if (st != ATTN_OK) return st;
+  if (groups == 0) return ATTN_OK;
+  if (!x || !cb || !dt || !dA_cumsum || !out) return ATTN_ERR_NULL_PTR;
+  const uintptr_t m = (uintptr_t)x | (uintptr_t)cb | (uintptr_t)dt | (uintptr_t)dA_cumsum | (uintptr_t)out;
+  if ((m & 15) != 0) return ATTN_ERR_MISALIGNED;
+  const int nc = (S + L - 1) / L;
+  hipLaunchKernelGGL((chunk_scan_fwd<4>), dim3((unsigned)groups), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)x, (const uint16_t*)cb, dt, dA_cumsum, out, S, H, L, nc);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -125,6 +125,26 @@ def test_bwd_validation_happens_before_any_hip_call(attn):
     assert call(N=0, q=0, dq=0, ws=0) == attn.ATTN_OK  # empty: nothing launched
 
 
+def test_chunk_scan_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20
+
+    def call(x=P, cb=P, dt=P, da=P, o=P, B=2, S=1000, H=8, Pd=64, L=256):
+        return attn.chunk_scan(x, cb, dt, da, o, B, S, H, Pd, L, None)
+
+    for kw in ("x", "cb", "dt", "da", "o"):
+        assert call(**{kw: 0}) == attn.ATTN_ERR_NULL_PTR, kw
+    assert call(Pd=128) == attn.ATTN_ERR_HEAD_DIM
+    for L in (0, 16, 48, 288, 512):
+        assert call(L=L) == attn.ATTN_ERR_BAD_SHAPE, L
+    assert call(S=-1) == attn.ATTN_ERR_BAD_SHAPE
+    assert call(H=0) == attn.ATTN_ERR_BAD_SHAPE
+    assert call(dt=P + 4) == attn.ATTN_ERR_MISALIGNED
+    assert call(x=P + 2) == attn.ATTN_ERR_MISALIGNED
+    big = 1 << 30
+    assert call(B=big, S=big) == attn.ATTN_ERR_BAD_SHAPE
+    assert call(S=0, x=0, o=0) == attn.ATTN_OK  # empty: nothing launched
+
+
 def test_variant_table(attn):
     n = attn.attn_num_variants()
     assert n >= 3

@@ -1,0 +1,120 @@
+"""Parity of the Mamba2 ChunkScan kernel (chunk_scan) with the fp64 oracle (GPU).
+
+Every call goes through the C ABI; inputs come from the seeded generator and
+expected values only from the oracle.
+
+Acceptance bar, relative to the reference's own scale:
+    max |out - ref|  <= 2e-2 * max |ref|  + 1e-5
+    mean |out - ref| <= 5e-3 * mean |ref| + 1e-5
+x and cb are exact bf16 and the products accumulate in fp32; the scaled
+matrix A = cb * exp(decay) * dt is rounded to bf16 (relative error up to
+2^-9 per term) before the contraction with x, which sets the relative terms;
+exp2 on v_exp_f32 adds about 1e-7.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from software_pipelined_amd import inputs as I
+
+from gpu_helpers import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+CS_MAX_REL = 2e-2
+CS_MEAN_REL = 5e-3
+CS_ABS_FLOOR = 1e-5
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    ensure_built()
+
+
+def _bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def run_cs(x, cb, dt, dacs, L):
+    import torch
+    from software_pipelined_amd import attn
+    out = attn.mamba_chunk_scan(_bf16(x), _bf16(cb), torch.from_numpy(dt).to("cuda"),
+                                torch.from_numpy(dacs).to("cuda"), L)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def compare(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got.astype(np.float64) - ref)
+    smax, smean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    emax, emean = float(err.max()), float(err.mean())
+    _say(f"{what}: max rel {emax / max(smax, 1e-30):.2e}, mean rel {emean / max(smean, 1e-30):.2e}")
+    assert emax <= CS_MAX_REL * smax + CS_ABS_FLOOR, f"{what}: max abs err {emax:.3e} vs {smax:.3e}"
+    assert emean <= CS_MEAN_REL * smean + CS_ABS_FLOOR, f"{what}: mean abs err {emean:.3e} vs {smean:.3e}"
+
+
+SHAPES = [
+    # (B, S, H, P, L)
+    (1, 1, 1, 64, 256),       # a single step
+    (1, 1000, 8, 64, 256),    # ragged last chunk (232 steps)
+    (2, 512, 4, 64, 256),
+    (1, 300, 2, 64, 128),     # two waves of the four idle in every chunk
+    (1, 64, 3, 64, 32),       # 32-step chunks: one block each
+    (2, 100, 5, 64, 64),
+    (1, 33, 2, 64, 32),       # ragged one-step last chunk
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b%d_s%d_h%d_p%d_l%d" % s)
+def test_chunk_scan_matches_oracle(oracle_mod, shape):
+    B, S, H, P, L = shape
+    _say(f"case chunk_scan {shape}")
+    x, cb, dt, dacs = I.gen_chunk_scan(B, S, H, P, L, seed=300 + S + H)
+    got = run_cs(x, cb, dt, dacs, L)
+    ref = oracle_mod.chunk_scan(x, cb, dt, dacs, L)
+    compare(got, ref, f"chunk_scan {shape}")
+
+
+def test_chunk_scan_small_workload(oracle_mod):
+    cfg = I.CHUNKSCAN_SMALL
+    _say(f"case chunk_scan workload {cfg.name}")
+    x, cb, dt, dacs = I.gen_chunk_scan_config(cfg)
+    compare(run_cs(x, cb, dt, dacs, cfg.L), oracle_mod.chunk_scan(x, cb, dt, dacs, cfg.L), cfg.name)
+
+
+def test_chunk_scan_b64_workload_sampled(oracle_mod):
+    """The BS=64 SEQ=8k workload at full size, as the benchmark launches it,
+    on sampled output rows (every chunk boundary of a few sequences plus
+    random rows)."""
+    cfg = I.CHUNKSCAN_B64
+    _say(f"case chunk_scan workload {cfg.name} (generating inputs)")
+    x, cb, dt, dacs = I.gen_chunk_scan_config(cfg)
+    got = run_cs(x, cb, dt, dacs, cfg.L).reshape(-1, cfg.P)
+    rng = np.random.default_rng(77)
+    rows = set(int(r) for r in rng.choice(cfg.B * cfg.S * cfg.H, size=3000, replace=False))
+    for b in (0, cfg.B - 1):
+        for c in range(cfg.nchunks):
+            for m in (0, 1, cfg.L - 1):
+                for h in (0, cfg.H - 1):
+                    rows.add((b * cfg.S + c * cfg.L + m) * cfg.H + h)
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = oracle_mod.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows)
+    compare(got[rows], ref, cfg.name)
+
+
+def test_chunk_scan_is_deterministic():
+    x, cb, dt, dacs = I.gen_chunk_scan(2, 700, 4, 64, 256, seed=5)
+    a = run_cs(x, cb, dt, dacs, 256)
+    b = run_cs(x, cb, dt, dacs, 256)
+    assert np.array_equal(a, b)
