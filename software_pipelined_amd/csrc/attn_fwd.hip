@@ -57,6 +57,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -1650,33 +1651,69 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
 // into the B-operand layout (so A never exists in memory) and x^T read from
 // an LDS image of the 32-step block with the transposing LDS read. One
 // workgroup per (b, chunk, h): 4 waves, wave w owns chunk rows 64w .. 64w+63;
-// the 32-step x blocks stream through a two-slot ring. Workgroup ids run
-// over heads fastest, so the heads sharing one cb chunk run together.
+// every input of a 32-step block (x, the cb columns, dt, dA_cumsum) streams
+// through a two-slot LDS ring, so the next block's loads are in flight while
+// this one is computed. Workgroup ids run over heads fastest, so the heads
+// sharing one cb chunk run together.
 constexpr int kCsP = 64;   // channels per head
-constexpr int kCsBK = 32;  // steps per x block
+constexpr int kCsBK = 32;  // steps per block
+// One ring slot: the x block (32 x 64 bf16, V layout), the cb columns of the
+// block for all 256 possible rows (64 bytes per row, 16-byte chunks XORed
+// with (row >> 1) & 3), then dt and dA_cumsum of the block's 32 steps (one
+// 1 KiB copy each, only the first 128 bytes used).
+constexpr int kCsX = kCsBK * kCsP * 2;
+constexpr int kCsCB = 256 * kCsBK * 2;
+constexpr int kCsSlot = kCsX + kCsCB + 2 * 1024;
 
-// Copy of x rows [row0, row0 + 32) of one (b, h) (row stride H*P) into an
-// LDS image in V layout: one 1 KiB instruction per wave; rows past the chunk
-// end read zeros.
-__device__ __forceinline__ void cs_copy_x(const uint16_t* xh, int row0, int rows_valid, int row_stride, char* dst,
-                                          int wave, int lane) {
-  const int pidx = wave * 64 + lane;
-  const int row = pidx >> 3, pc = pidx & 7;
-  const int c = pc ^ swz_v<kCsP>(row);
-  const int bytes = __builtin_amdgcn_readfirstlane((rows_valid - 1) * row_stride * 2 + kCsP * 2);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(xh + (size_t)row0 * row_stride), (short)0, bytes, kRsrcWord3);
-  LDS_AS void* to = (LDS_AS void*)(dst + wave * 64 * 16);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to, 16, row * row_stride * 2 + c * 16, 0, 0, 0);
+// 16 bytes per lane into LDS at lds_wave_base + 16 * lane, hidden from the
+// compiler's wait tracking (callers wait with wait_vmcnt).
+__device__ __forceinline__ void cs_dma(__amdgpu_buffer_rsrc_t r, int voff, char* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "s"(m0)
+               : "m0", "memory");
+}
+
+// All copies of block j (steps k0 = 32j ..): x rows (rows past the chunk
+// read zeros), the cb columns k0 .. k0+31 of rows k0 .. L-1 (earlier rows
+// never see the block), dt and dA_cumsum.
+template <int NW>
+__device__ __forceinline__ void cs_copy_block(const uint16_t* xh, const uint16_t* cbc, const float* dtc,
+                                              const float* dac, int j, int Lc, int L, int row_stride, char* slot,
+                                              int wave, int lane) {
+  const int k0 = j * kCsBK;
+  {  // x: one 1 KiB copy per wave (8 rows)
+    const int pidx = wave * 64 + lane;
+    const int row = pidx >> 3, pc = pidx & 7;
+    const int rows_valid = min(kCsBK, Lc - k0);
+    const int bytes = __builtin_amdgcn_readfirstlane((rows_valid - 1) * row_stride * 2 + kCsP * 2);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xh + (size_t)k0 * row_stride), (short)0, bytes, kRsrcWord3);
+    cs_dma(r, row * row_stride * 2 + ((pc ^ swz_v<kCsP>(row)) << 4), slot + wave * 1024);
+  }
+  {  // cb: (L - k0) rows of 64 bytes = (L - k0) / 16 copies of 1 KiB, dealt over the waves
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cbc, (short)0, L * L * 2, kRsrcWord3);
+    const int n = (L - k0) / 16;
+    for (int t = wave; t < n; t += NW) {
+      const int pidx = t * 64 + lane;
+      const int row = k0 + (pidx >> 2), pc = pidx & 3;
+      const int c = pc ^ ((row >> 1) & 3);
+      cs_dma(r, (row * L + k0) * 2 + (c << 4), slot + kCsX + k0 * 64 + t * 1024);
+    }
+  }
+  if (wave == 0) {  // dt and dA_cumsum of the block's 32 steps
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dtc + k0), (short)0, 128, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(dac + k0), (short)0, 128, kRsrcWord3);
+    cs_dma(rd, lane * 16, slot + kCsX + kCsCB);
+    cs_dma(ra, lane * 16, slot + kCsX + kCsCB + 1024);
+  }
 }
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __restrict__ X, const uint16_t* __restrict__ CB,
                                                          const float* __restrict__ DT, const float* __restrict__ DAC,
                                                          float* __restrict__ OUT, int S, int H, int L, int nc) {
-  static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block");
-  constexpr int XB = kCsBK * kCsP * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * XB];
+  static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block; 4 x 64 rows = 256");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kCsSlot];
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % H, c = (blockIdx.x / H) % nc, b = blockIdx.x / (H * nc);
@@ -1700,38 +1737,41 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
 #pragma unroll
     for (int t = 0; t < kCsP / 32; ++t) o[qt][t] = f32x16{};
 
-  cs_copy_x(xh, 0, min(kCsBK, Lc), row_stride, smem, wave, lane);
+  cs_copy_block<NW>(xh, cbc, dtc, dac, 0, Lc, L, row_stride, smem, wave, lane);
   for (int j = 0; j < nblk; ++j) {
     wait_vmcnt<0>();
     block_barrier();
     if (j + 1 < nblk)
-      cs_copy_x(xh, (j + 1) * kCsBK, min(kCsBK, Lc - (j + 1) * kCsBK), row_stride, smem + ((j + 1) & 1) * XB, wave,
-                lane);
+      cs_copy_block<NW>(xh, cbc, dtc, dac, j + 1, Lc, L, row_stride, smem + ((j + 1) & 1) * kCsSlot, wave, lane);
     const int k0 = j * kCsBK;
     if (mw >= Lc || k0 > mw + 63) continue;  // wave-uniform: no row of this wave sees the block
+    const char* slot = smem + (j & 1) * kCsSlot;
+    const char* cbs = slot + kCsX;
+    const char* dts = cbs + kCsCB;
     // dt and dA_cumsum of this lane's 16 steps: k0 + 16hf + 8e + 4hl + i
     f32x4 dtv[2][2], dav[2][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        dtv[hf][e] = *(const f32x4*)(dtc + k0 + 16 * hf + 8 * e + 4 * hl);
-        dav[hf][e] = *(const f32x4*)(dac + k0 + 16 * hf + 8 * e + 4 * hl);
+        dtv[hf][e] = *(LDS_AS const f32x4*)(dts + (16 * hf + 8 * e + 4 * hl) * 4);
+        dav[hf][e] = *(LDS_AS const f32x4*)(dts + 1024 + (16 * hf + 8 * e + 4 * hl) * 4);
       }
     bf16x8 pb[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int m = mw + 32 * qt + (lane & 31);
-      const uint16_t* cbr = cbc + (size_t)min(m, L - 1) * L + k0 + 4 * hl;
+      const int sw = (m >> 1) & 3;
+      const char* cbr = cbs + m * 64 + 8 * hl;  // rows below k0 hold stale data; their terms are masked
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         float a[8];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const uint2 raw = *(const uint2*)(cbr + 16 * hf + 8 * e);
+          const u32x2 raw = *(LDS_AS const u32x2*)(cbr + (((2 * hf + e) ^ sw) << 4));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint32_t w = i < 2 ? raw.x : raw.y;
+            const uint32_t w = raw[i >> 1];
             const float cbv = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
             const int kk = k0 + 16 * hf + 8 * e + 4 * hl + i;
             const float decay = __builtin_amdgcn_exp2f((dam[qt] - dav[hf][e][i]) * kLog2e);
@@ -1742,7 +1782,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
                             (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
       }
     }
-    pv_block<kCsP, kCsBK, 2>(smem + (j & 1) * XB, off, pb, o);
+    pv_block<kCsP, kCsBK, 2>(slot, off, pb, o);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
 #pragma unroll
