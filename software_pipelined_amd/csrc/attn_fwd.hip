@@ -1662,8 +1662,11 @@ constexpr int kCsBK = 32;  // steps per block
 // with (row >> 1) & 3), then dt and dA_cumsum of the block's 32 steps (one
 // 1 KiB copy each, only the first 128 bytes used).
 constexpr int kCsX = kCsBK * kCsP * 2;
-constexpr int kCsCB = 256 * kCsBK * 2;
-constexpr int kCsSlot = kCsX + kCsCB + 2 * 1024;
+template <int RW>
+struct CsSlot {
+  static constexpr int CB = RW * kCsBK * 2;    // cb columns of the block for the workgroup's RW rows
+  static constexpr int BYTES = kCsX + CB + 2 * 1024;
+};
 
 // 16 bytes per lane into LDS at lds_wave_base + 16 * lane, hidden from the
 // compiler's wait tracking (callers wait with wait_vmcnt).
@@ -1674,12 +1677,13 @@ __device__ __forceinline__ void cs_dma(__amdgpu_buffer_rsrc_t r, int voff, char*
 }
 
 // All copies of block j (steps k0 = 32j ..): x rows (rows past the chunk
-// read zeros), the cb columns k0 .. k0+31 of rows k0 .. L-1 (earlier rows
-// never see the block), dt and dA_cumsum.
-template <int NW>
+// read zeros), the cb columns k0 .. k0+31 of the workgroup's rows
+// [max(k0, r0), min(L, r0 + RW)) (earlier rows never see the block), dt and
+// dA_cumsum.
+template <int NW, int RW>
 __device__ __forceinline__ void cs_copy_block(const uint16_t* xh, const uint16_t* cbc, const float* dtc,
-                                              const float* dac, int j, int Lc, int L, int row_stride, char* slot,
-                                              int wave, int lane) {
+                                              const float* dac, int j, int Lc, int L, int r0, int row_stride,
+                                              char* slot, int wave, int lane) {
   const int k0 = j * kCsBK;
   {  // x: one 1 KiB copy per wave (8 rows)
     const int pidx = wave * 64 + lane;
@@ -1690,64 +1694,71 @@ __device__ __forceinline__ void cs_copy_block(const uint16_t* xh, const uint16_t
         __builtin_amdgcn_make_buffer_rsrc((void*)(xh + (size_t)k0 * row_stride), (short)0, bytes, kRsrcWord3);
     cs_dma(r, row * row_stride * 2 + ((pc ^ swz_v<kCsP>(row)) << 4), slot + wave * 1024);
   }
-  {  // cb: (L - k0) rows of 64 bytes = (L - k0) / 16 copies of 1 KiB, dealt over the waves
+  {  // cb: rows of 64 bytes, 16 per 1 KiB copy, dealt over the waves
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cbc, (short)0, L * L * 2, kRsrcWord3);
-    const int n = (L - k0) / 16;
+    const int first = max(k0, r0), n = (min(L, r0 + RW) - first) / 16;
     for (int t = wave; t < n; t += NW) {
       const int pidx = t * 64 + lane;
-      const int row = k0 + (pidx >> 2), pc = pidx & 3;
+      const int row = first + (pidx >> 2), pc = pidx & 3;
       const int c = pc ^ ((row >> 1) & 3);
-      cs_dma(r, (row * L + k0) * 2 + (c << 4), slot + kCsX + k0 * 64 + t * 1024);
+      cs_dma(r, (row * L + k0) * 2 + (c << 4), slot + kCsX + (first - r0) * 64 + t * 1024);
     }
   }
   if (wave == 0) {  // dt and dA_cumsum of the block's 32 steps
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dtc + k0), (short)0, 128, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(dac + k0), (short)0, 128, kRsrcWord3);
-    cs_dma(rd, lane * 16, slot + kCsX + kCsCB);
-    cs_dma(ra, lane * 16, slot + kCsX + kCsCB + 1024);
+    cs_dma(rd, lane * 16, slot + kCsX + CsSlot<RW>::CB);
+    cs_dma(ra, lane * 16, slot + kCsX + CsSlot<RW>::CB + 1024);
   }
 }
 
-template <int NW>
+// QT 32-row tiles per wave: a workgroup covers RW = 32*QT*NW chunk rows
+// starting at r0; a chunk takes ceil(L / RW) workgroups.
+template <int NW, int QT>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __restrict__ X, const uint16_t* __restrict__ CB,
                                                          const float* __restrict__ DT, const float* __restrict__ DAC,
                                                          float* __restrict__ OUT, int S, int H, int L, int nc) {
-  static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block; 4 x 64 rows = 256");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kCsSlot];
+  static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block");
+  constexpr int RW = 32 * QT * NW;
+  constexpr int SLOT = CsSlot<RW>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x % H, c = (blockIdx.x / H) % nc, b = blockIdx.x / (H * nc);
-  const int c0 = c * L, Lc = min(L, S - c0);
-  const int nblk = (Lc + kCsBK - 1) / kCsBK;
+  const int nparts = (L + RW - 1) / RW;
+  const int h = blockIdx.x % H, part = (blockIdx.x / H) % nparts, c = (blockIdx.x / (H * nparts)) % nc,
+            b = blockIdx.x / (H * nparts * nc);
+  const int c0 = c * L, Lc = min(L, S - c0), r0 = part * RW;
+  if (r0 >= Lc) return;  // workgroup-uniform: this part of a short last chunk is empty
+  const int nblk = (min(Lc, r0 + RW) + kCsBK - 1) / kCsBK;
   const int row_stride = H * kCsP;
   const uint16_t* xh = X + ((size_t)b * S + c0) * row_stride + (size_t)h * kCsP;
   const uint16_t* cbc = CB + ((size_t)b * nc + c) * L * L;
   const size_t sc = (((size_t)b * H + h) * nc + c) * L;
   const float* dtc = DT + sc;
   const float* dac = DAC + sc;
-  const int mw = 64 * wave;  // first chunk row of this wave
+  const int mw = r0 + 32 * QT * wave;  // first chunk row of this wave
 
-  float dam[2];
+  float dam[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) dam[qt] = dac[min(mw + 32 * qt + (lane & 31), Lc - 1)];
+  for (int qt = 0; qt < QT; ++qt) dam[qt] = dac[min(mw + 32 * qt + (lane & 31), Lc - 1)];
   const LdsOffsets<kCsP> off(lane);
-  f32x16 o[2][kCsP / 32];
+  f32x16 o[QT][kCsP / 32];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int t = 0; t < kCsP / 32; ++t) o[qt][t] = f32x16{};
 
-  cs_copy_block<NW>(xh, cbc, dtc, dac, 0, Lc, L, row_stride, smem, wave, lane);
+  cs_copy_block<NW, RW>(xh, cbc, dtc, dac, 0, Lc, L, r0, row_stride, smem, wave, lane);
   for (int j = 0; j < nblk; ++j) {
     wait_vmcnt<0>();
     block_barrier();
     if (j + 1 < nblk)
-      cs_copy_block<NW>(xh, cbc, dtc, dac, j + 1, Lc, L, row_stride, smem + ((j + 1) & 1) * kCsSlot, wave, lane);
+      cs_copy_block<NW, RW>(xh, cbc, dtc, dac, j + 1, Lc, L, r0, row_stride, smem + ((j + 1) & 1) * SLOT, wave, lane);
     const int k0 = j * kCsBK;
-    if (mw >= Lc || k0 > mw + 63) continue;  // wave-uniform: no row of this wave sees the block
-    const char* slot = smem + (j & 1) * kCsSlot;
+    if (mw >= Lc || k0 > mw + 32 * QT - 1) continue;  // wave-uniform: no row of this wave sees the block
+    const char* slot = smem + (j & 1) * SLOT;
     const char* cbs = slot + kCsX;
-    const char* dts = cbs + kCsCB;
+    const char* dts = cbs + CsSlot<RW>::CB;
     // dt and dA_cumsum of this lane's 16 steps: k0 + 16hf + 8e + 4hl + i
     f32x4 dtv[2][2], dav[2][2];
 #pragma unroll
@@ -1757,12 +1768,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
         dtv[hf][e] = *(LDS_AS const f32x4*)(dts + (16 * hf + 8 * e + 4 * hl) * 4);
         dav[hf][e] = *(LDS_AS const f32x4*)(dts + 1024 + (16 * hf + 8 * e + 4 * hl) * 4);
       }
-    bf16x8 pb[2][2];
+    bf16x8 pb[QT][2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const int m = mw + 32 * qt + (lane & 31);
       const int sw = (m >> 1) & 3;
-      const char* cbr = cbs + m * 64 + 8 * hl;  // rows below k0 hold stale data; their terms are masked
+      const char* cbr = cbs + (m - r0) * 64 + 8 * hl;  // rows below k0 hold stale data; their terms are masked
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         float a[8];
@@ -1782,11 +1793,11 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
                             (__bf16)a[4], (__bf16)a[5], (__bf16)a[6], (__bf16)a[7]};
       }
     }
-    pv_block<kCsP, kCsBK, 2>(slot, off, pb, o);
+    pv_block<kCsP, kCsBK, QT>(slot, off, pb, o);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int m = mw + 32 * qt + (lane & 31);
     if (m < Lc) {
       float* orow = OUT + (((size_t)b * S + c0 + m) * H + h) * kCsP;
@@ -2066,7 +2077,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
 }
 
 // ChunkScan: P = 64 channels per head; chunk length a multiple of 32, at most
-// 256 (four waves of 64 rows).
+// 256; a workgroup of four waves covers kCsRows rows of a chunk.
+constexpr int kCsRows = 128;
 int chunk_scan_check(int B, int S, int H, int P, int L, long long* groups) {
   if (B < 0 || S < 0 || H < 1) return ATTN_ERR_BAD_SHAPE;
   if (P != kCsP) return ATTN_ERR_HEAD_DIM;
@@ -2210,7 +2222,10 @@ int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_c
   const uintptr_t m = (uintptr_t)x | (uintptr_t)cb | (uintptr_t)dt | (uintptr_t)dA_cumsum | (uintptr_t)out;
   if ((m & 15) != 0) return ATTN_ERR_MISALIGNED;
   const int nc = (S + L - 1) / L;
-  hipLaunchKernelGGL((chunk_scan_fwd<4>), dim3((unsigned)groups), dim3(256), 0, (hipStream_t)stream,
+  const long long parts = (L + kCsRows - 1) / kCsRows;
+  if (groups * parts > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL((chunk_scan_fwd<4, kCsRows / 128>), dim3((unsigned)(groups * parts)), dim3(256), 0,
+                     (hipStream_t)stream,
                      (const uint16_t*)x, (const uint16_t*)cb, dt, dA_cumsum, out, S, H, L, nc);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
