@@ -1,6 +1,6 @@
 /*
- * Attention (forward, decoding, backward) and Mamba2 ChunkScan oracle: plain,
- * slow, fp64 CPU reference.
+ * Attention (forward, decoding, backward, MLA decoding) and Mamba2 ChunkScan
+ * oracle: plain, slow, fp64 CPU reference.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
@@ -367,6 +367,70 @@ int oracle_chunk_scan_rows(const uint16_t* x, const uint16_t* cb, const float* d
   }
   (void)threads;
   return 0;
+}
+
+/*
+ * MLA decoding (multi-head latent attention, the decoding operator the
+ * PipeThreader-and-TileLang page cites as a short TileLang program), in the
+ * absorbed form: every query head attends to one shared cache of latent
+ * rows; a row's first Dv values are its value, all Dk values its key.
+ *   q  : bf16 bits [B][H][Dk];   kv : bf16 bits [B][N][Dk]
+ *   s_hj = sigma * q_h . kv_j;  P = softmax_j;  out_h = sum_j P_hj kv_j[0:Dv]
+ *   lse_h = ln sum_j exp(s_hj)
+ *   rows : flat (b*H + h) ids, NULL = all;  out [n_rows][Dv], lse [n_rows]
+ */
+int oracle_mla_decode_rows(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t H, int64_t N, int64_t Dk,
+                           int64_t Dv, float scale, const int64_t* rows, int64_t n_rows, double* out,
+                           double* lse, int threads) {
+  if (B < 0 || H < 0 || N < 1 || Dk < 1 || Dv < 1 || Dv > Dk) return -1;
+  int64_t total = B * H;
+  if (rows == NULL) n_rows = total;
+  if (n_rows == 0) return 0;
+  if (!q || !kv || !out || !lse) return -1;
+  for (int64_t t = 0; rows && t < n_rows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return -1;
+  const double sg = scale;  /* the float32 scale, widened exactly */
+  int bad = 0;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel num_threads(threads) reduction(+ : bad)
+#endif
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)N);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+    for (int64_t t = 0; t < n_rows; ++t) {
+      int64_t r = rows ? rows[t] : t;
+      const uint16_t* qh = q + r * Dk;
+      const uint16_t* kvb = kv + (r / H) * N * Dk;
+      double m = -INFINITY;
+      for (int64_t j = 0; j < N; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) dot += widen_bf16(qh[c]) * widen_bf16(kvb[j * Dk + c]);
+        w[j] = sg * dot;
+        if (w[j] > m) m = w[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < N; ++j) {
+        w[j] = exp(w[j] - m);
+        l += w[j];
+      }
+      double* o = out + t * Dv;
+      for (int64_t c = 0; c < Dv; ++c) o[c] = 0.0;
+      double psum = 0.0;
+      for (int64_t j = 0; j < N; ++j) {
+        const double p = w[j] / l;
+        psum += p;
+        for (int64_t c = 0; c < Dv; ++c) o[c] += p * widen_bf16(kvb[j * Dk + c]);
+      }
+      lse[t] = m + log(l);
+      bad += fabs(psum - 1.0) <= 1e-12 ? 0 : 1;
+    }
+    free(w);
+  }
+  (void)threads;
+  return bad;
 }
 
 /* Number of threads an OpenMP region would use by default (1 without OpenMP). */

@@ -1,5 +1,5 @@
 """Python access to the fp64 oracle (``attn_oracle.c``): attention forward,
-decoding and backward, and Mamba2 ChunkScan.
+decoding, backward and MLA decoding, and Mamba2 ChunkScan.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path. It loads the C
@@ -79,6 +79,12 @@ def bind(path: str):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.oracle_mla_decode_rows.restype = ctypes.c_int
+    lib.oracle_mla_decode_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -251,3 +257,36 @@ def chunk_scan(x, cb, dt, dacs, L: int, threads: int = 0, lib=None):
     """fp64 ChunkScan over every row: out [B, S, H, P]."""
     return chunk_scan_rows(x, cb, dt, dacs, L, None, threads, lib).reshape(x.shape)
 
+
+def mla_decode_rows(q, kv, Dv: int, scale, rows=None, threads: int = 0, lib=None):
+    """fp64 MLA decoding: q [B, H, Dk] against one shared cache kv [B, N, Dk]
+    (keys: all Dk values of a row; values: its first Dv). ``rows``: flat
+    (b*H + h) ids or None. Returns (out [n_rows, Dv], lse [n_rows]) float64."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    if q.ndim != 3 or kv.ndim != 3 or q.shape[0] != kv.shape[0] or q.shape[2] != kv.shape[2]:
+        raise ValueError("q must be [B, H, Dk] and kv [B, N, Dk]")
+    B, H, Dk = q.shape
+    N = kv.shape[1]
+    if rows is None:
+        n_rows, rows_ptr = B * H, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows, rows_ptr = rows.size, rows.ctypes.data
+    out = np.empty((n_rows, Dv), dtype=np.float64)
+    lse = np.empty((n_rows,), dtype=np.float64)
+    rc = (lib or _load()).oracle_mla_decode_rows(q.ctypes.data, kv.ctypes.data, B, H, N, Dk, Dv,
+                                                 float(np.float32(scale)), rows_ptr, n_rows, out.ctypes.data,
+                                                 lse.ctypes.data, int(threads))
+    if rc < 0:
+        raise ValueError("oracle rejected its arguments")
+    if rc > 0:
+        raise ArithmeticError(f"{rc} softmax rows failed the sum-to-one self-check")
+    return out, lse
+
+
+def mla_decode(q, kv, Dv: int, scale, threads: int = 0, lib=None):
+    """fp64 MLA decoding over every head: (out [B, H, Dv], lse [B, H])."""
+    B, H, _ = q.shape
+    out, lse = mla_decode_rows(q, kv, Dv, scale, None, threads, lib)
+    return out.reshape(B, H, Dv), lse.reshape(B, H)

@@ -159,6 +159,49 @@ CHUNKSCAN_B64 = ChunkScanConfig("chunkscan_b64_s8192_h64_p64_l256", 64, 8192, 64
 CHUNKSCAN_CONFIGS = [CHUNKSCAN_SMALL, CHUNKSCAN_B64]
 
 
+@dataclass(frozen=True)
+class MlaConfig:
+    """One MLA decoding workload: per sequence, H query heads of Dk = 576
+    (512 latent + 64 rotary) values attend to one shared cache of N latent
+    rows whose first Dv = 512 values are the value (the absorbed form of
+    DeepSeek-V2/V3 attention: 128 heads, latent 512, rotary 64), decoded at
+    the pages' decode batch sizes 1 and 32 against a 4096-row cache."""
+
+    name: str
+    B: int
+    H: int
+    N: int
+    seed: int
+    Dk: int = 576
+    Dv: int = 512
+
+    @property
+    def scale(self) -> np.float32:
+        # DeepSeek's softmax scale: 1/sqrt(128 + 64) for 128 no-rope and 64 rope channels per head
+        return np.float32(1.0 / np.sqrt(192.0))
+
+    def flops(self) -> int:
+        return 2 * self.B * self.H * self.N * (self.Dk + self.Dv)
+
+    def hbm_bytes(self) -> int:
+        """Compulsory: bf16 q and cache read once, fp32 out and lse written once."""
+        return 2 * self.B * (self.H + self.N) * self.Dk + 4 * self.B * self.H * (self.Dv + 1)
+
+
+def gen_mla(B: int, H: int, N: int, Dk: int, seed: int):
+    """(q [B, H, Dk], kv [B, N, Dk]) as bf16 bits, N(0, 1), q then kv from
+    ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, H, Dk), dtype=np.float32))
+    kv = f32_to_bf16_bits(rng.standard_normal((B, N, Dk), dtype=np.float32))
+    return q, kv
+
+
+MLA_B1 = MlaConfig("mla_b1_h128_n4096_dk576_dv512", 1, 128, 4096, seed=31)
+MLA_B32 = MlaConfig("mla_b32_h128_n4096_dk576_dv512", 32, 128, 4096, seed=32)
+MLA_CONFIGS = [MLA_B1, MLA_B32]
+
+
 DECODE_B1 = DecodeConfig("decode_b1_h32_nq1_nkv4096_d128", 1, 32, 1, 4096, 128, seed=11)
 DECODE_B32 = DecodeConfig("decode_b32_h32_nq1_nkv4096_d128", 32, 32, 1, 4096, 128, seed=12)
 DECODE_CONFIGS = [DECODE_B1, DECODE_B32]
