@@ -413,8 +413,9 @@ int oracle_mla_decode_rows(const uint16_t* q, const uint16_t* kv, int64_t B, int
       }
       double l = 0.0;
       for (int64_t j = 0; j < N; ++j) {
-        w[j] = exp(w[j] - m);
-        l += w[j];
+        const double e = exp(w[j] - m);
+        w[j] = e;
+        l += e;
       }
       double* o = out + t * Dv;
       for (int64_t c = 0; c < Dv; ++c) o[c] = 0.0;
