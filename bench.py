@@ -24,6 +24,9 @@ step = one call (three kernels), rate = 10*N^2*d*B*H algorithmic flops
 --chunkscan times the Mamba2 ChunkScan entry (chunk_scan) on a ChunkScan
 workload: one step = one call, rate = compulsory HBM bytes per second.
 
+--mla times MLA decoding (mla_decode) on an MLA workload: one step = one call
+(two kernels), rate = compulsory HBM bytes per second, MFMA rate beside it.
+
 --decode times the split-KV decoding entry (attn_fwd_decode) on a decode
 workload instead: one step = one call (partial kernel + merge kernel), and the
 rate is compulsory HBM bytes per second against MI355X's 8 TB/s.
@@ -318,6 +321,82 @@ def chunkscan_bench(args):
         "cpu_baseline": cpu}), flush=True)
 
 
+def mla_bench(args):
+    """MLA decoding (mla_decode): reports compulsory HBM bytes per second (the
+    shared cache read once) with the achieved MFMA rate beside it."""
+    import numpy as np
+    import torch
+
+    from software_pipelined_amd import attn, inputs
+
+    cfgs = {c.name: c for c in inputs.MLA_CONFIGS}
+    cfg = cfgs[args.workload] if args.workload else inputs.MLA_B32
+    log(f"mla workload {cfg.name}: generating inputs")
+    q, kv = inputs.gen_mla(cfg.B, cfg.H, cfg.N, cfg.Dk, cfg.seed)
+    dev = torch.device("cuda:0")
+    tq, tkv = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev) for a in (q, kv))
+    out = torch.empty((cfg.B, cfg.H, cfg.Dv), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device=dev)
+    st, need = attn.mla_decode_workspace_size(cfg.B, cfg.H, cfg.N)
+    if st != 0:
+        raise attn.AttnError(st)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    args_c = (tq.data_ptr(), tkv.data_ptr(), out.data_ptr(), lse.data_ptr(), cfg.B, cfg.H, cfg.N, float(cfg.scale),
+              ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def step():
+        st = attn.mla_decode(*args_c)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(args.steps):
+        step()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    mean_ms = float(np.mean(durs))
+    nbytes = cfg.hbm_bytes()
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    tflops = cfg.flops() / (mean_ms * 1e-3) / 1e12
+    log(f"{cfg.name}: call mean {mean_ms * 1e3:.1f} us, median {float(np.median(durs)) * 1e3:.1f} us; {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}); {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS:.0f})")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attn_oracle
+        attn_oracle.build(force=False)
+        threads = attn_oracle.max_threads()
+        rows = np.arange(min(cfg.B * cfg.H, 64 * threads))
+        t1 = time.perf_counter()
+        attn_oracle.mla_decode_rows(q, kv, cfg.Dv, cfg.scale, rows, threads=threads)
+        dt_s = time.perf_counter() - t1
+        cpu = {"value": cfg.hbm_bytes() * rows.size / (cfg.B * cfg.H) / dt_s / 1e9, "unit": "GB/s",
+               "cores": int(threads), "kind": "oracle",
+               "sample": f"first {rows.size} of {cfg.B * cfg.H} head rows, fp64 C oracle, {dt_s:.1f} s wall"}
+    print(json.dumps({
+        "metric": "MLA decode: compulsory HBM bytes per second (q and the shared latent cache read once; out, lse "
+                  "written)",
+        "value": round(nbytes * args.steps / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "Dk": cfg.Dk, "Dv": cfg.Dv,
+                   "bytes_per_step": nbytes, "flops_per_step": cfg.flops(), "workspace_bytes": need},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "call_us_mean": round(mean_ms * 1e3, 2), "call_us_median": round(float(np.median(durs)) * 1e3, 2)},
+        "cpu_baseline": cpu}), flush=True)
+
+
 def sweep(cfg, attn, ptrs, out, lse, stream, args):
     """Time every variant for cfg's head dim. Parity gate: a variant's output
     must equal, bit for bit, that of the double-buffered simple schedule with
@@ -469,6 +548,8 @@ def main():
     ap.add_argument("--chunkscan", action="store_true",
                     help="time the Mamba2 ChunkScan entry (chunk_scan) on a ChunkScan workload instead "
                          "(HBM-bound: reports GB/s of compulsory traffic)")
+    ap.add_argument("--mla", action="store_true",
+                    help="time MLA decoding (mla_decode) on an MLA workload instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -509,6 +590,9 @@ def main():
         return
     if args.chunkscan:
         chunkscan_bench(args)
+        return
+    if args.mla:
+        mla_bench(args)
         return
 
     cfg = inputs.HEADLINE

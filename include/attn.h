@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused attention library (libattn.so):
- * forward, split-KV decoding and backward, and Mamba2 ChunkScan. Plain C
- * types only; no C++ or framework types cross it.
+ * forward, split-KV decoding, backward and MLA decoding, and Mamba2
+ * ChunkScan. Plain C types only; no C++ or framework types cross it.
  *
  * The operation (PipeThreader, OSDI'25 summary page, "FlashAttention-3"
  * paragraph and Fig 7; "PipeThreader and TileLang" page, section 4.1): for
@@ -190,6 +190,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* out, cons
  */
 int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_cumsum, float* out, int B, int S,
                int H, int P, int L, void* stream);
+
+/*
+ * MLA decoding (multi-head latent attention in the absorbed form; the
+ * decoding operator the PipeThreader-and-TileLang page cites as a short
+ * TileLang program). Every query head of sequence b attends to one shared
+ * cache of N latent rows of 576 values (512 latent + 64 rotary); a row's
+ * first 512 values are its value:
+ *     s_hj = scale * q_h . kv_j (576 products),  out_h = softmax_j(s_h) kv[:, 0:512],
+ *     lse_h = ln sum_j exp(s_hj).
+ *
+ *   q   : device, bf16, [B][H][576];   kv : device, bf16, [B][N][576]
+ *   out : device, float32, [B][H][512]; lse : device, float32, [B][H]; fully overwritten
+ *   H   : a multiple of 64 (else ATTN_ERR_BAD_SHAPE); N >= 1 when B*H > 0
+ *   scale : finite, nonzero float32
+ *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
+ *           aligned, at least mla_decode_workspace_size bytes (else
+ *           ATTN_ERR_WORKSPACE); contents on entry do not matter
+ *   stream : hipStream_t (NULL = default stream); two kernels are enqueued
+ *
+ * Same ownership, validation and asynchrony rules as attn_fwd_decode; the
+ * library allocates nothing; calls sharing one workspace must not overlap.
+ */
+int mla_decode_workspace_size(int B, int H, int N, size_t* bytes);
+int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int H, int N, float scale,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,10 +1,10 @@
 """Thin Python binding of ``libattn.so`` (C ABI declared in include/attn.h).
 
-Argument marshalling only: every step of the attention forward, decoding and
-backward and of the Mamba2 ChunkScan runs in the HIP kernels. The low-level functions take raw device
+Argument marshalling only: every step of the attention forward, decoding,
+backward and MLA decoding and of the Mamba2 ChunkScan runs in the HIP kernels. The low-level functions take raw device
 pointers and sizes with the same names and argument order as the C entry
-points; ``attn_forward``, ``attn_decode``, ``attn_backward`` and
-``mamba_chunk_scan`` are
+points; ``attn_forward``, ``attn_decode``, ``attn_backward``,
+``mla_decode_torch`` and ``mamba_chunk_scan`` are
 convenience wrappers that allocate outputs (and workspaces) with torch
 (device memory and streams are all torch is used for) and call them.
 
@@ -72,6 +72,11 @@ def load_library():
     lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_decode_workspace_size.restype = ctypes.c_int
+    lib.mla_decode_workspace_size.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_decode.restype = ctypes.c_int
+    lib.mla_decode.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 3 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.chunk_scan.restype = ctypes.c_int
     lib.chunk_scan.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
@@ -189,6 +194,46 @@ def attn_backward(q, k, v, out, lse, dout, causal: bool = False, scale=None, dq=
     if st != ATTN_OK:
         raise AttnError(st)
     return dq, dk, dv
+
+
+def mla_decode_workspace_size(B, H, N):
+    """(status, bytes) as returned through the C ``mla_decode_workspace_size``."""
+    n = ctypes.c_size_t(0)
+    st = load_library().mla_decode_workspace_size(B, H, N, ctypes.byref(n))
+    return st, n.value
+
+
+def mla_decode(q, kv, out, lse, B, H, N, scale, workspace, workspace_bytes, stream) -> int:
+    """Same arguments as the C ``mla_decode``: device pointers (ints), sizes, stream."""
+    return load_library().mla_decode(q, kv, out, lse, B, H, N, float(scale), workspace, workspace_bytes, stream)
+
+
+def mla_decode_torch(q, kv, scale, out=None, lse=None, workspace=None, stream=None):
+    """MLA decoding for torch tensors: q bfloat16 [B, H, 576], kv bfloat16
+    [B, N, 576] (values: the first 512 of each row). Returns (out float32
+    [B, H, 512], lse float32 [B, H])."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or q.dim() != 3 or kv.dim() != 3:
+        raise ValueError("q [B, H, 576] and kv [B, N, 576] must be bfloat16")
+    B, H, Dk = q.shape
+    N = kv.shape[1]
+    if Dk != 576 or kv.shape[0] != B or kv.shape[2] != 576 or not q.is_contiguous() or not kv.is_contiguous():
+        raise ValueError("q [B, H, 576] and kv [B, N, 576], contiguous")
+    st, need = mla_decode_workspace_size(B, H, N)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=q.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = mla_decode(q.data_ptr(), kv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, scale,
+                    workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse
 
 
 def chunk_scan(x, cb, dt, dA_cumsum, out, B, S, H, P, L, stream) -> int:

@@ -145,6 +145,27 @@ def test_chunk_scan_validation_happens_before_any_hip_call(attn):
     assert call(S=0, x=0, o=0) == attn.ATTN_OK  # empty: nothing launched
 
 
+def test_mla_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20
+    st, need = attn.mla_decode_workspace_size(32, 128, 4096)
+    assert st == attn.ATTN_OK and need > 0 and need % (4 * 513) == 0
+    assert attn.mla_decode_workspace_size(0, 128, 4096) == (attn.ATTN_OK, 0)
+    assert attn.mla_decode_workspace_size(1, 96, 4096)[0] == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.mla_decode_workspace_size(1, 128, 0)[0] == attn.ATTN_ERR_BAD_SHAPE
+
+    def call(q=P, kv=P, o=P, l=P, B=32, H=128, N=4096, s=0.07, ws=P, wsb=None):
+        return attn.mla_decode(q, kv, o, l, B, H, N, s, ws, need if wsb is None else wsb, None)
+
+    for kw in ("q", "kv", "o", "l", "ws"):
+        assert call(**{kw: 0}) == attn.ATTN_ERR_NULL_PTR, kw
+    assert call(H=64 + 32) == attn.ATTN_ERR_BAD_SHAPE
+    assert call(s=float("nan")) == attn.ATTN_ERR_BAD_SCALE
+    assert call(kv=P + 8) == attn.ATTN_ERR_MISALIGNED
+    assert call(l=P + 2) == attn.ATTN_ERR_MISALIGNED
+    assert call(wsb=need - 1) == attn.ATTN_ERR_WORKSPACE
+    assert call(B=0, q=0, kv=0, o=0, l=0, ws=0) == attn.ATTN_OK
+
+
 def test_variant_table(attn):
     n = attn.attn_num_variants()
     assert n >= 3
