@@ -1823,8 +1823,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
 // one LDS image of a 32-row block serves both S^T = K Q^T (row fragments) and
 // O^T += V^T P^T (transposed reads of its first 512 columns). Four waves:
 // wave = 2*tile + half takes the 32 heads of its tile and output dims
-// [256*half, 256*half + 256); both waves of a tile form the same S (the 576-
-// wide Q^T stays in AGPRs, the 256-wide O^T half in VGPRs).
+// [256*half, 256*half + 256); the two waves of a tile split the 576-wide
+// contraction of S (288 each, their Q^T halves in AGPRs) and swap partial
+// sums through LDS, so both hold the same S (a + b == b + a exactly).
 constexpr int kMlaDk = 576, kMlaDv = 512, kMlaBN = 32;
 constexpr int kMlaRow = kMlaDk * 2;             // bytes per cache row
 constexpr int kMlaBlock = kMlaBN * kMlaRow;     // 36 KiB per 32-row block
@@ -1847,12 +1848,15 @@ __device__ __forceinline__ void mla_copy_block(const uint16_t* kvb, int row0, in
 }
 
 // Grid: (B * H/64) x NC. Chunk c of the key blocks as chunk_begin.
+constexpr int kMlaHalfK = kMlaDk / 32;  // 16-wide contraction steps per wave (18)
+constexpr int kMlaXchg = 4 * 64 * 64;     // partial-S exchange: 64 bytes per lane per wave
+
 __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
                                                             const uint16_t* __restrict__ KV,
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
                                                             int N, int H, int nc, float c_log2, int negate_q) {
   static_assert(kMlaCopies % 4 == 0, "copies split evenly over four waves");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kMlaBlock];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kMlaBlock + kMlaXchg];
   const int lane = threadIdx.x & 63, hl = lane >> 5, lq = lane & 31, ci = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = wave >> 1, half = wave & 1;
@@ -1874,23 +1878,27 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     if (half == 0 && hl == 0) ws_lse[(size_t)c * rows + row] = -INFINITY;
     return;
   }
-  // Q^T fragments (B operand): lane holds q[head h0 + lq][16kk + 8hl .. +7]
-  bf16x8 qf[1][kMlaDk / 16];
+  // Q^T fragments of this wave's contraction half (B operand): lane holds
+  // q[head h0 + lq][16(kh + kk) + 8hl .. +7], kh = 18 half
+  const int kh = kMlaHalfK * half;
+  bf16x8 qf[1][kMlaHalfK];
   {
-    const uint16_t* qp = Q + row * kMlaDk + 8 * hl;
+    const uint16_t* qp = Q + row * kMlaDk + 16 * kh + 8 * hl;
 #pragma unroll
-    for (int kk = 0; kk < kMlaDk / 16; ++kk) {
+    for (int kk = 0; kk < kMlaHalfK; ++kk) {
       u32x4 raw = *(const u32x4*)(qp + kk * 16);
       if (negate_q) raw ^= 0x80008000u;
       qf[0][kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  park_in_agprs<1, kMlaDk / 16>(qf);
+  park_in_agprs<1, kMlaHalfK>(qf);
+  char* xmine = smem + 2 * kMlaBlock + wave * 4096 + lane * 16;
+  const char* xother = smem + 2 * kMlaBlock + (wave ^ 1) * 4096 + lane * 16;
   // row-fragment offsets: chunk 2kk + hl of row lq = 128 (kk >> 2) + 16 (2 (kk & 3) ^ e0)
   const int e0 = hl ^ (lq & 7);
-  int kq[4];
+  int kq[4];  // indexed by (kk - kh) & 3: step kk of this wave's half has kk & 3 = (i + (kh & 3)) & 3
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) kq[q4] = lq * kMlaRow + 16 * ((2 * q4) ^ e0);
+  for (int q4 = 0; q4 < 4; ++q4) kq[q4] = lq * kMlaRow + 16 * ((2 * ((q4 + (kh & 3)) & 3)) ^ e0);
   // transposed-read offsets (as LdsOffsets::v): row r0 + 16p + 8r, dims
   // 256 half + 32t + 16g2 + 4(ci & 3); the swizzle depends on r0 only
   const int r0 = 4 * hl + (ci >> 2), c1 = 2 * ((lane >> 4) & 1) + ((ci & 3) >> 1);
@@ -1911,9 +1919,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     f32x16 s[1][1];
     s[0][0] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < kMlaDk / 16; ++kk)
-      s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(LDS_AS const bf16x8*)(Ks + kq[kk & 3] + 128 * (kk >> 2)),
-                                                        qf[0][kk], s[0][0], 0, 0, 0);
+    for (int i = 0; i < kMlaHalfK; ++i) {
+      const int kk = kh + i;  // runtime only through kh (0 or 18)
+      s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *(LDS_AS const bf16x8*)(Ks + kq[i & 3] + 128 * (kk >> 2)), qf[0][i], s[0][0], 0, 0, 0);
+    }
+    // swap the partial sums with the other wave of the tile
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(LDS_AS f32x4*)(xmine + g * 1024) = f32x4{s[0][0][4 * g], s[0][0][4 * g + 1], s[0][0][4 * g + 2], s[0][0][4 * g + 3]};
+    block_barrier();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 o4 = *(LDS_AS const f32x4*)(xother + g * 1024);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[0][0][4 * g + e] += o4[e];
+    }
     if ((j + 1) * kMlaBN > N) mask_block<kMlaBN, 1, false>(s, j * kMlaBN, 0, N, lane);
     bf16x8 pb[1][2];
     softmax_block<kMlaBN, 1>(s, pb, c_log2, m_run, l_run, alpha);
@@ -2265,8 +2286,8 @@ int chunk_scan_check(int B, int S, int H, int P, int L, long long* groups) {
 }
 
 // MLA decoding: H a multiple of 64 (64 heads per workgroup); chunks sized so
-// that about two resident rounds of workgroups (one per CU) cover the cache,
-// at least two 32-row blocks per chunk.
+// that one resident round of workgroups (one per CU) covers the cache, at
+// least two 32-row blocks per chunk.
 struct MlaPlan {
   int nc;
   long long groups, rows;
@@ -2287,8 +2308,8 @@ int mla_plan(int B, int H, int N, MlaPlan* p) {
       p->rows > INT_MAX)
     return ATTN_ERR_BAD_SHAPE;
   const long long nblk = (N + kMlaBN - 1) / kMlaBN;
-  long long nc = (2 * 256 + p->groups - 1) / p->groups;
-  nc = std::min(nc, std::max(1LL, nblk / 2));
+  long long nc = (256 + p->groups - 1) / p->groups;  // one resident round (one workgroup per CU)
+  nc = std::min(nc, std::max(1LL, nblk / 2));  // at least two blocks per chunk
   nc = std::min(nc, (long long)kDecodeMaxChunks);
   long long floats = 0;
   if (__builtin_mul_overflow(nc * p->rows, (long long)(kMlaDv + 1), &floats) || floats > (1LL << 40) ||
