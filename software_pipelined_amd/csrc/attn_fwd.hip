@@ -1849,6 +1849,7 @@ __device__ __forceinline__ void mla_copy_block(const uint16_t* kvb, int row0, in
 
 // Grid: (B * H/64) x NC. Chunk c of the key blocks as chunk_begin.
 constexpr int kMlaHalfK = kMlaDk / 32;  // 16-wide contraction steps per wave (18)
+constexpr int kMlaST = 3;                 // ring slots: two blocks in flight behind the one in use
 constexpr int kMlaXchg = 4 * 64 * 64;     // partial-S exchange: 64 bytes per lane per wave
 
 __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
@@ -1856,7 +1857,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
                                                             int N, int H, int nc, float c_log2, int negate_q) {
   static_assert(kMlaCopies % 4 == 0, "copies split evenly over four waves");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kMlaBlock + kMlaXchg];
+  __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg];
   const int lane = threadIdx.x & 63, hl = lane >> 5, lq = lane & 31, ci = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = wave >> 1, half = wave & 1;
@@ -1892,8 +1893,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     }
   }
   park_in_agprs<1, kMlaHalfK>(qf);
-  char* xmine = smem + 2 * kMlaBlock + wave * 4096 + lane * 16;
-  const char* xother = smem + 2 * kMlaBlock + (wave ^ 1) * 4096 + lane * 16;
+  char* xmine = smem + kMlaST * kMlaBlock + wave * 4096 + lane * 16;
+  const char* xother = smem + kMlaST * kMlaBlock + (wave ^ 1) * 4096 + lane * 16;
   // row-fragment offsets: chunk 2kk + hl of row lq = 128 (kk >> 2) + 16 (2 (kk & 3) ^ e0)
   const int e0 = hl ^ (lq & 7);
   int kq[4];  // indexed by (kk - kh) & 3: step kk of this wave's half has kk & 3 = (i + (kh & 3)) & 3
@@ -1910,12 +1911,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
   for (int t = 0; t < 8; ++t) o[0][t] = f32x16{};
   float m_run[1] = {-INFINITY}, l_run[1] = {0.f}, alpha[1];
 
-  mla_copy_block(kvb, b0 * kMlaBN, N, smem, wave, lane);
+  // blocks j .. j+ST-2 are in flight at the top of block j; every iteration
+  // issues one block's copies (past the chunk end a duplicate of its last
+  // block lands in the free slot), so the count of younger copies is exact
+  constexpr int PER_BLOCK = kMlaCopies / 4;
+#pragma unroll
+  for (int i = 0; i < kMlaST - 1; ++i)
+    mla_copy_block(kvb, min(b0 + i, b1 - 1) * kMlaBN, N, smem + i * kMlaBlock, wave, lane);
   for (int j = b0; j < b1; ++j) {
-    wait_vmcnt<0>();
+    const int jr = j - b0;
+    wait_vmcnt<(kMlaST - 2) * PER_BLOCK>();
     block_barrier();
-    if (j + 1 < b1) mla_copy_block(kvb, (j + 1) * kMlaBN, N, smem + ((j + 1 - b0) & 1) * kMlaBlock, wave, lane);
-    const char* Ks = smem + ((j - b0) & 1) * kMlaBlock;
+    mla_copy_block(kvb, min(j + kMlaST - 1, b1 - 1) * kMlaBN, N, smem + ((jr + kMlaST - 1) % kMlaST) * kMlaBlock,
+                   wave, lane);
+    const char* Ks = smem + (jr % kMlaST) * kMlaBlock;
     f32x16 s[1][1];
     s[0][0] = f32x16{};
 #pragma unroll
