@@ -1978,7 +1978,15 @@ __global__ __launch_bounds__(256, 1) void mla_combine(const float* __restrict__ 
                                                      float* __restrict__ O, float* __restrict__ LSE, int rows, int nc) {
   __shared__ float w_sh[kDecodeMaxChunks];
   __shared__ float red[8];
+  constexpr int PF = 8;  // partials per thread and dim loaded before the weights are known
   const int tid = threadIdx.x, row = blockIdx.x;
+  float p0[PF], p1[PF];
+#pragma unroll
+  for (int c = 0; c < PF; ++c) {
+    const float* src = ws_o + ((size_t)min(c, nc - 1) * rows + row) * kMlaDv;
+    p0[c] = src[tid];
+    p1[c] = src[tid + 256];
+  }
   float mx = -INFINITY;
   for (int c = tid; c < nc; c += 256) {
     const float l = ws_lse[(size_t)c * rows + row];
@@ -2002,7 +2010,13 @@ __global__ __launch_bounds__(256, 1) void mla_combine(const float* __restrict__ 
   __syncthreads();  // also publishes every weight in w_sh
   const float wsum = (red[4] + red[5]) + (red[6] + red[7]);
   float a0 = 0.f, a1 = 0.f;
-  for (int c = 0; c < nc; ++c) {
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+    if (c < nc) {
+      a0 += w_sh[c] * p0[c];
+      a1 += w_sh[c] * p1[c];
+    }
+  for (int c = PF; c < nc; ++c) {
     const float* src = ws_o + ((size_t)c * rows + row) * kMlaDv;
     a0 += w_sh[c] * src[tid];
     a1 += w_sh[c] * src[tid + 256];
