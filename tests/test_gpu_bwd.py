@@ -156,6 +156,22 @@ def test_bwd_workload_16k_sampled(oracle_mod):
     _sampled_parity(oracle_mod, cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, cfg.seed, (cfg.B * cfg.H - 1,), cfg.name)
 
 
+def test_bwd_workload_d64_causal_8k_sampled(oracle_mod):
+    """The causal N=8192 d=64 workload with every 7th key scaled by 8, at full
+    size as the benchmark times it: dQ on sampled rows of every head, dK and
+    dV on sampled key rows of the first and last heads."""
+    cfg = I.CAUSAL_8K_STRESS
+    _say(f"case bwd workload {cfg.name}")
+    q, k, v = I.gen_config(cfg)
+    do = I.gen_dout(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed)
+    got = [x.reshape(-1, cfg.d) for x in run_bwd(q, k, v, do, cfg.causal, cfg.scale)]
+    qrows = I.sample_rows(cfg.B, cfg.H, cfg.N, per_head=3, seed=51)
+    heads = (0, cfg.B * cfg.H - 1)
+    krows = np.concatenate([h * cfg.N + I.sample_rows(1, 1, cfg.N, per_head=16, seed=52 + h) for h in heads])
+    dq, dk, dv = oracle_mod.attn_bwd_rows(q, k, v, do, cfg.causal, cfg.scale, qrows, krows)
+    compare_grads((got[0][qrows], got[1][krows], got[2][krows]), (dq, dk, dv), cfg.name)
+
+
 def test_bwd_reuses_one_workspace(oracle_mod):
     import torch
     from software_pipelined_amd import attn
