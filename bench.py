@@ -49,7 +49,8 @@ METRIC = "attention fwd TFLOP/s (bf16) and % of MI355X MFMA peak, N=16384 d=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "software_pipelined_amd", "csrc", "attn_fwd.hip")
+# the forward kernels and the device helpers they are built from
+KERNEL_SRCS = [os.path.join(ROOT, "software_pipelined_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.h")]
 
 
 def log(*a):
@@ -57,7 +58,10 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

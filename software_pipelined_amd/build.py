@@ -1,6 +1,8 @@
 """Build step for the HIP library ``libattn.so`` (gfx950 only).
 
-Compiles ``csrc/attn_fwd.hip`` with hipcc into ``software_pipelined_amd/libattn.so``.
+Compiles the kernel sources in ``csrc/`` (attention forward, split-KV decoding,
+backward, Mamba2 ChunkScan, MLA decoding; shared device helpers in
+``attn_common.h``) with one hipcc call into ``software_pipelined_amd/libattn.so``.
 Packed FP32 VALU forms are disabled for all device code.
 """
 
@@ -12,7 +14,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in
+        ("attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "chunk_scan.hip", "mla_decode.hip")]
 LIB = os.path.join(PKG, "libattn.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
@@ -36,7 +39,7 @@ def compile_cmd(out: str, extra=()) -> list:
             # every block for the VALU rescale; the Q fragments are parked in
             # AGPRs explicitly instead
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            *extra, SRC, "-o", out]
+            *extra, *SRCS, "-o", out]
 
 
 def build_library(verbose: bool = False) -> str:

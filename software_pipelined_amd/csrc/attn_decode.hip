@@ -1,0 +1,300 @@
+// attn_decode.hip -- split-KV decoding (attn_fwd_decode) on MI355X (gfx950).
+//
+// Part of libattn.so; the C ABI is declared in include/attn.h.
+
+#include "attn_common.h"
+
+namespace {
+
+// ---------------------------------------------------------------- split-KV decoding
+// Decoding step (split-KV / FlashDecoding in the pages' microbenchmarks):
+// Nq query rows per (batch, head) against a cache of Nkv keys, every query
+// seeing every key. Few query rows leave the matrix cores nearly idle, so the
+// work is split over the keys instead: the key blocks of one (batch, head,
+// 32-row query tile) are dealt to NC chunks, each processed by one wave with
+// its own online softmax (the same per-block steps as the forward kernels) and
+// written as a normalised partial (O_c, LSE_c) to the caller's workspace. A
+// second kernel merges the chunks of each row: LSE = ln sum_c exp(LSE_c),
+// O = sum_c exp(LSE_c - LSE) O_c. The pass is HBM-bound (K and V are read
+// once), so each wave streams its own chunk through a private LDS ring and
+// never waits on the other waves of its workgroup.
+
+// HBM -> LDS copy issued through inline assembly. The compiler's wait
+// analysis does not treat the transposing LDS reads as disjoint from an
+// in-flight copy, and would wait for every outstanding copy before each V
+// read (no overlap of the next block's copy with this block's math); hidden
+// from it, the copies are waited for explicitly (wait_vmcnt) instead. The
+// memory clobber keeps LDS reads of the slot being overwritten in program
+// order before the copy.
+template <int D, int BN, bool IS_V>
+__device__ __forceinline__ void issue_copy_wave(const uint16_t* __restrict__ src, int row0, int N, char* dst,
+                                                int lane, int t) {
+  const __amdgpu_buffer_rsrc_t r = block_rsrc<D, BN>(src, row0, N);
+  const int off = (int)block_lane_offset<D, 1, BN, IS_V>(t, 0, lane);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)(dst + t * 64 * 16);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "s"(m0)
+               : "m0", "memory");
+}
+
+template <int D, int BN>
+__device__ __forceinline__ void copy_block_wave(const uint16_t* Kh, const uint16_t* Vh, int row0, int N,
+                                                char* ks, char* vs, int lane) {
+  constexpr int LD = Tile<D, 1, BN>::LOADS;
+#pragma unroll
+  for (int t = 0; t < LD; ++t) {
+    issue_copy_wave<D, BN, false>(Kh, row0, N, ks, lane, t);
+    issue_copy_wave<D, BN, true>(Vh, row0, N, vs, lane, t);
+  }
+}
+
+
+// Grid: (B*H*n_qt) x (NC / NW) workgroups of NW waves; wave w of workgroup
+// (x, y) takes chunk y*NW + w of query tile x % n_qt of head x / n_qt.
+template <int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int BH, int Nq, int Nkv, int n_qt, int nc,
+    float c_log2, int negate_q) {
+  constexpr int ST = 2;
+  constexpr int MAT = BN * D * 2;
+  constexpr int PER_BLOCK = 2 * Tile<D, 1, BN>::LOADS;
+  __shared__ __attribute__((aligned(1024))) char smem[NW * ST * 2 * MAT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bh = blockIdx.x / n_qt, qt0 = (blockIdx.x % n_qt) * 32;
+  const int c = blockIdx.y * NW + wave;
+  const int nblk = (Nkv + BN - 1) / BN;
+  const int b0 = chunk_begin(c, nblk, nc), b1 = chunk_begin(c + 1, nblk, nc);
+  const uint16_t* Kh = K + (size_t)bh * Nkv * D;
+  const uint16_t* Vh = V + (size_t)bh * Nkv * D;
+  char* ring = smem + wave * (ST * 2 * MAT);
+  auto ks = [ring](int s) { return ring + s * MAT; };
+  auto vs = [ring](int s) { return ring + (ST + s) * MAT; };
+
+  bf16x8 qf[1][D / 16];
+  load_q<D, 1>(Q + (size_t)bh * Nq * D, qt0, Nq, negate_q, qf, lane);
+  if constexpr (NW <= 4) park_in_agprs<1, D / 16>(qf);
+  const LdsOffsets<D> off(lane);
+  f32x16 o[1][D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) o[0][t] = f32x16{};
+  float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
+
+  if (b0 == b1) {  // an empty chunk (fewer key blocks than chunks): weight zero in the merge
+    const int qi = qt0 + (lane & 31);
+    if (qi < Nq) {
+      float* orow = ws_o + ((size_t)c * BH * Nq + (size_t)bh * Nq + qi) * D;
+      for (int e = (lane >> 5); e < D; e += 2) orow[e] = 0.f;
+      if (lane < 32) ws_lse[(size_t)c * BH * Nq + (size_t)bh * Nq + qi] = -INFINITY;
+    }
+    return;
+  }
+  copy_block_wave<D, BN>(Kh, Vh, b0 * BN, Nkv, ks(0), vs(0), lane);
+  for (int j = b0; j < b1; ++j) {
+    const int slot = (j - b0) & 1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the slot about to be refilled are done
+    if (j + 1 < b1) {
+      copy_block_wave<D, BN>(Kh, Vh, (j + 1) * BN, Nkv, ks(slot ^ 1), vs(slot ^ 1), lane);
+      wait_vmcnt<PER_BLOCK>();  // block j has landed, block j+1 may stay in flight
+    } else {
+      wait_vmcnt<0>();
+    }
+    const char* kslot = ks(slot);
+    const char* vslot = vs(slot);
+    f32x16 s[1][BN / 32];
+    qk_block<D, BN, 1>(kslot, off, qf, s);
+    sched_mfma_with_reads<(D / 16) * (BN / 32), 1, 1, kPfQK>();
+    const int kv0 = j * BN;
+    if (kv0 + BN > Nkv) mask_block<BN, 1, false>(s, kv0, 0, Nkv, lane);
+    bf16x8 pb[1][BN / 16];
+    float alpha[1];
+    softmax_block<BN, 1>(s, pb, c_log2, m_run, l_run, alpha);
+    rescale_block<D, 1>(o, alpha);
+    pv_block<D, BN, 1>(vslot, off, pb, o);
+    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, 1, kPfPV>();
+  }
+  wait_vmcnt<0>();  // no copy into LDS may outlive the wave
+  store_rows<D, 1>(ws_o + (size_t)c * BH * Nq * D, ws_lse + (size_t)c * BH * Nq, (size_t)bh * Nq * D,
+                   (size_t)bh, Nq, qt0 + (lane & 31), o, m_run, l_run, lane);
+}
+
+// One workgroup per query row merges the row's NC chunk partials: the chunk
+// weights exp(LSE_c - max) are formed once in LDS, while each thread already
+// holds its first partials in registers; each thread sums one output
+// dimension over a slice of the chunks (coalesced across threads) and the
+// slices are added in LDS.
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __restrict__ ws_o,
+                                                             const float* __restrict__ ws_lse,
+                                                             float* __restrict__ O, float* __restrict__ LSE,
+                                                             int rows, int nc) {
+  constexpr int G = 256 / D;  // chunk slices
+  __shared__ float w_sh[kDecodeMaxChunks];
+  __shared__ float red[256];
+  constexpr int PF = 32;      // partials per thread loaded before the weights are known
+  const int tid = threadIdx.x, row = blockIdx.x;
+  const int dim = tid % D, g = tid / D;
+  float pre[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int c = g + i * G;
+    pre[i] = c < nc ? ws_o[((size_t)c * rows + row) * D + dim] : 0.f;
+  }
+  float mx = -INFINITY;
+  for (int c = tid; c < nc; c += 256) {
+    const float l = ws_lse[(size_t)c * rows + row];
+    w_sh[c] = l;
+    mx = fmaxf(mx, l);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float ws = 0.f;
+  for (int c = tid; c < nc; c += 256) {
+    const float w = __builtin_amdgcn_exp2f((w_sh[c] - mx) * kLog2e);  // 0 for an empty chunk
+    w_sh[c] = w;
+    ws += w;
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) ws += __shfl_xor(ws, sh);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = ws;
+  __syncthreads();  // also publishes every weight in w_sh
+  const float wsum = (red[4] + red[5]) + (red[6] + red[7]);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int c = g + i * G;
+    if (c < nc) acc += w_sh[c] * pre[i];
+  }
+  int c = g + PF * G;
+  for (; c + 3 * G < nc; c += 4 * G) {
+    const float* src = ws_o + ((size_t)c * rows + row) * D + dim;
+    const size_t st = (size_t)G * rows * D;
+    acc += w_sh[c] * src[0] + w_sh[c + G] * src[st] + w_sh[c + 2 * G] * src[2 * st] +
+           w_sh[c + 3 * G] * src[3 * st];
+  }
+  for (; c < nc; c += G) acc += w_sh[c] * ws_o[((size_t)c * rows + row) * D + dim];
+  __syncthreads();  // every thread has read red[4..7]
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float o = red[tid];
+#pragma unroll
+    for (int k = 1; k < G; ++k) o += red[tid + k * D];
+    O[(size_t)row * D + tid] = o / wsum;
+  }
+  if (tid == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
+}
+
+// Split-KV decoding: 32-key blocks, 4 waves per workgroup (2 at d = 256,
+// whose 64 KiB ring per wave fills the LDS). Each wave's K/V ring holds
+// 2 slots x 2 matrices x 32 keys x d bf16, so the 160 KiB LDS of a CU keeps
+// 8 waves resident at d = 64, 4 at d = 128 and 2 at d = 256; the chunks are
+// sized so that one resident round of waves (256 CUs) streams the cache,
+// rounded up to a multiple of the waves per workgroup.
+constexpr int kDecodeBN = 32;
+constexpr int kDecodeCUs = 256;
+constexpr int kDecodeLdsPerCU = 160 * 1024;
+
+constexpr int decode_waves(int d, int nw) {
+  return kDecodeCUs * (kDecodeLdsPerCU / (nw * 2 * 2 * kDecodeBN * d * 2)) * nw;
+}
+static_assert(decode_waves(64, 4) == 2048 && decode_waves(128, 4) == 1024 && decode_waves(256, 2) == 512,
+              "resident decode waves");
+static_assert(decode_waves(64, 4) <= kDecodeMaxChunks, "chunk bound of the merge");
+
+struct DecodePlan {
+  int n_qt, nw, nc;
+  long long rows;   // B*H*Nq
+  size_t ws_bytes;  // nc * rows * (d + 1) floats
+};
+
+int decode_plan(int B, int H, int Nq, int Nkv, int d, DecodePlan* p) {
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEAD_DIM;
+  long long bh = 0, rows = 0, elems_q = 0, rows_kv = 0, elems_kv = 0;
+  if (__builtin_mul_overflow((long long)B, (long long)H, &bh) ||
+      __builtin_mul_overflow(bh, (long long)Nq, &rows) ||
+      __builtin_mul_overflow(rows, (long long)d, &elems_q) ||
+      __builtin_mul_overflow(bh, (long long)Nkv, &rows_kv) ||
+      __builtin_mul_overflow(rows_kv, (long long)d, &elems_kv))
+    return ATTN_ERR_BAD_SHAPE;
+  p->rows = rows;
+  p->nw = d == 256 ? 2 : 4;
+  p->n_qt = (Nq + 31) / 32;
+  p->nc = 0;
+  p->ws_bytes = 0;
+  if (rows == 0) return ATTN_OK;
+  if (Nkv < 1) return ATTN_ERR_BAD_SHAPE;  // a query with no key has no softmax
+  const long long groups = bh * p->n_qt;
+  if (elems_q > (1LL << 50) || elems_kv > (1LL << 50) || groups > INT_MAX || rows > INT_MAX)
+    return ATTN_ERR_BAD_SHAPE;
+  const long long nblk = (Nkv + kDecodeBN - 1) / kDecodeBN;
+  const long long waves = decode_waves(d, p->nw);
+  long long want = (waves + groups - 1) / groups;
+  if (want > nblk) want = nblk;
+  const long long nc = ((want + p->nw - 1) / p->nw) * p->nw;  // <= waves <= kDecodeMaxChunks
+  long long floats = 0;
+  if (__builtin_mul_overflow(nc * rows, (long long)(d + 1), &floats) || floats > (1LL << 40))
+    return ATTN_ERR_BAD_SHAPE;
+  p->nc = (int)nc;
+  p->ws_bytes = (size_t)floats * sizeof(float);
+  return ATTN_OK;
+}
+
+template <int D, int NW>
+hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, const void* v, float* out,
+                         float* lse, int BH, int Nq, int Nkv, float scale, void* ws, hipStream_t stream) {
+  const float c = fabsf(scale) * kLog2e;
+  const int neg = scale < 0.f;
+  float* ws_o = (float*)ws;
+  float* ws_lse = ws_o + (size_t)p.nc * p.rows * D;
+  const dim3 grid((unsigned)(BH * p.n_qt), (unsigned)(p.nc / NW)), block(NW * 64);
+  hipLaunchKernelGGL((attn_decode_partial<D, NW, kDecodeBN>), grid, block, 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o, ws_lse, BH, Nq,
+                     Nkv, p.n_qt, p.nc, c, neg);
+  const int rows = (int)p.rows;
+  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)rows), dim3(256), 0, stream,
+                     (const float*)ws_o, (const float*)ws_lse, out, lse, rows, p.nc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_workspace_size(int B, int H, int Nq, int Nkv, int d, size_t* bytes) {
+  DecodePlan p;
+  const int st = decode_plan(B, H, Nq, Nkv, d, &p);
+  if (st == ATTN_OK && bytes) *bytes = p.ws_bytes;
+  return st;
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
+                    int Nq, int Nkv, int d, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  DecodePlan p;
+  int st = decode_plan(B, H, Nq, Nkv, d, &p);
+  if (st != ATTN_OK) return st;
+  uint32_t sbits;
+  memcpy(&sbits, &scale, sizeof sbits);
+  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
+  if (p.rows == 0) return ATTN_OK;
+  if (!q || !k || !v || !out || !lse || !workspace) return ATTN_ERR_NULL_PTR;
+  const uintptr_t m = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)workspace;
+  if ((m & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_MISALIGNED;
+  if (workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+  const int BH = B * H;
+  hipError_t e;
+  switch (d) {
+    case 64: e = launch_decode<64, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
+    case 128: e = launch_decode<128, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
+    default: e = launch_decode<256, 2>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"
