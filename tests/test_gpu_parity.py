@@ -88,6 +88,22 @@ def test_full_size_workloads_sampled_rows(oracle_mod, cfg):
     _say(f"{cfg.name} rows={rows.size} {stats}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_sequence_sampled_rows(oracle_mod, d):
+    """A sequence 8x the longest workload (N = 131072, one head): the block
+    loop runs 1024-2048 blocks and row and element offsets pass 2^24; checked
+    on sampled rows, both masks."""
+    N = 1 << 17
+    q, k, v = I.gen_qkv(1, 1, N, d, seed=2024 + d)
+    for causal in (False, True):
+        _say(f"case long N{N} d{d} causal={causal}")
+        out, lse = run_gpu(q, k, v, causal, I.default_scale(d))
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        rows = I.sample_rows(1, 1, N, per_head=48, seed=d)
+        ro, rl = oracle_mod.attn_fwd_rows(q, k, v, causal, I.default_scale(d), rows)
+        compare(out.reshape(-1, d)[rows], lse.reshape(-1)[rows], ro, rl, f"long N{N} d{d} causal={causal}")
+
+
 def test_every_variant_matches_oracle(oracle_mod):
     from software_pipelined_amd import attn
     for vid in range(attn.attn_num_variants()):
