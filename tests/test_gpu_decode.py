@@ -71,6 +71,19 @@ def test_decode_workloads_all_rows(oracle_mod, cfg):
     _say(str(compare(out, lse, ro, rl, cfg.name)))
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 1, 100000, 64), (1, 8, 2, 131072, 128)],
+                         ids=lambda s: "b%d_h%d_nq%d_nkv%d_d%d" % s)
+def test_decode_long_caches(oracle_mod, shape):
+    """Long caches: one head of d = 64 takes the largest chunk count the merge
+    handles (2048 chunks); 8 heads of d = 128 against 131072 keys."""
+    B, H, Nq, Nkv, d = shape
+    _say(f"case decode long cache {shape}")
+    q, k, v = I.gen_decode(B, H, Nq, Nkv, d, seed=31 + d)
+    out, lse = run_decode(q, k, v, I.default_scale(d))
+    ro, rl = oracle_mod.attn_decode(q, k, v, I.default_scale(d))
+    _say(str(compare(out, lse, ro, rl, f"decode {shape}")))
+
+
 def test_decode_negative_scale_and_stress_keys(oracle_mod):
     # a negative scale, and every 7th key scaled by 8 (near-one-hot rows)
     B, H, Nq, Nkv, d = 2, 2, 2, 700, 64
