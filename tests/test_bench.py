@@ -56,3 +56,28 @@ def test_committed_traffic_record_is_consistent():
         n = cfg.B * cfg.H * cfg.N
         assert ent["compulsory_bytes_per_launch"] == 3 * n * cfg.d * 2 + n * cfg.d * 4 + n * 4
         assert ent["hbm_bytes_per_launch"] >= ent["compulsory_bytes_per_launch"]
+
+
+def test_other_rows_algorithmic_counts():
+    """The work and byte counts the other bench modes divide by, against
+    brute-force counts on small shapes."""
+    # ChunkScan: causal pairs inside each chunk, ragged last chunk included
+    cs = I.ChunkScanConfig("t", 2, 70, 3, 64, 32, seed=1)
+    brute = sum(1 for s in range(cs.S) for k in range(cs.S) if k // cs.L == s // cs.L and k <= s)
+    assert cs.pairs() == brute
+    assert cs.flops() == 2 * cs.B * cs.H * cs.P * brute
+    nc = 3
+    assert cs.hbm_bytes() == (2 * 2 * 70 * 3 * 64 + 2 * 2 * nc * 32 * 32 + 2 * 4 * 2 * 3 * nc * 32
+                              + 4 * 2 * 70 * 3 * 64)
+    # backward: five contractions over the visible pairs, 2.5x the forward's two
+    for cfg in I.CONFIGS:
+        assert 2 * I.bwd_flops(cfg) == 5 * cfg.flops()
+    # decoding: q, k, v read once in bf16, out and lse written once in fp32
+    dc = I.DecodeConfig("t", 3, 4, 2, 100, 64, seed=1)
+    assert dc.kv_bytes() == 2 * (3 * 4 * 2 * 64 + 2 * 3 * 4 * 100 * 64) + 4 * 3 * 4 * 2 * 65
+    assert dc.flops() == 4 * 3 * 4 * 2 * 100 * 64
+    # MLA: q and the shared cache read once, out (512 wide) and lse written once
+    m = I.MlaConfig("t", 2, 64, 10, seed=1)
+    assert m.hbm_bytes() == 2 * (2 * 64 * 576 + 2 * 10 * 576) + 4 * 2 * 64 * 513
+    assert m.flops() == 2 * 2 * 64 * 10 * (576 + 512)
+
