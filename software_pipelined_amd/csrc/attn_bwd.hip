@@ -70,22 +70,14 @@ __device__ __forceinline__ bf16x8 read_tr_k(const char* img, const BwdOffsets<D>
 template <int D, int NW, int BN>
 __device__ __forceinline__ void issue_copy_asm(const uint16_t* __restrict__ src, int row0, int N, char* dst,
                                                int wave, int lane, int t) {
-  const __amdgpu_buffer_rsrc_t r = block_rsrc<D, BN>(src, row0, N);
-  const int off = (int)block_lane_offset<D, NW, BN, false>(t, wave, lane);
-  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)(dst + (t * NW + wave) * 64 * 16);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "s"(m0)
-               : "m0", "memory");
+  cs_dma(block_rsrc<D, BN>(src, row0, N), (int)block_lane_offset<D, NW, BN, false>(t, wave, lane),
+         dst + (t * NW + wave) * 64 * 16);
 }
 
 // One 256-byte statistics block into a wave's own 1 KiB LDS slot (lanes past
 // the block read zeros).
 __device__ __forceinline__ void issue_stat_copy(const float* src, char* dst, int lane) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBwdStatBytes, kRsrcWord3);
-  const int off = lane * 16;
-  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)dst;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "s"(m0)
-               : "m0", "memory");
+  cs_dma(__builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBwdStatBytes, kRsrcWord3), lane * 16, dst);
 }
 
 // stats[bh][blk] = { log2e * LSE of the block's 32 rows, D of those rows };

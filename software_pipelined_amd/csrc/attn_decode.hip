@@ -19,21 +19,13 @@ namespace {
 // once), so each wave streams its own chunk through a private LDS ring and
 // never waits on the other waves of its workgroup.
 
-// HBM -> LDS copy issued through inline assembly. The compiler's wait
-// analysis does not treat the transposing LDS reads as disjoint from an
-// in-flight copy, and would wait for every outstanding copy before each V
-// read (no overlap of the next block's copy with this block's math); hidden
-// from it, the copies are waited for explicitly (wait_vmcnt) instead. The
-// memory clobber keeps LDS reads of the slot being overwritten in program
-// order before the copy.
+// HBM -> LDS copy t of a wave-private block (cs_dma: inline assembly, so the
+// compiler's conservative wait before the transposing V reads does not drain
+// the next block's copy; the copies are waited for with wait_vmcnt).
 template <int D, int BN, bool IS_V>
 __device__ __forceinline__ void issue_copy_wave(const uint16_t* __restrict__ src, int row0, int N, char* dst,
                                                 int lane, int t) {
-  const __amdgpu_buffer_rsrc_t r = block_rsrc<D, BN>(src, row0, N);
-  const int off = (int)block_lane_offset<D, 1, BN, IS_V>(t, 0, lane);
-  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)(dst + t * 64 * 16);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "s"(m0)
-               : "m0", "memory");
+  cs_dma(block_rsrc<D, BN>(src, row0, N), (int)block_lane_offset<D, 1, BN, IS_V>(t, 0, lane), dst + t * 64 * 16);
 }
 
 template <int D, int BN>
