@@ -50,11 +50,32 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the forward kernels and the device helpers they are built from
-KERNEL_SRCS = [os.path.join(ROOT, "software_pipelined_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "software_pipelined_amd", "csrc", f)
+               for f in ("attn_fwd_kernels.h", "attn_fwd_variants.h", "attn_fwd_d64.hip", "attn_fwd_d128.hip",
+                         "attn_fwd_d256.hip", "attn_common.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, and the
+    CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 0
+    return {"cpu_model": model, "nproc": os.cpu_count() or 0, "usable_cpus": usable}
 
 
 def kernel_source_hash() -> str:
@@ -101,7 +122,7 @@ def cpu_baseline(cfg, q, k, v, target_s: float):
         flops = float(sum(4 * cfg.d * (int(r % cfg.N) + 1) for r in rows))
     else:
         flops = float(per_row_flops * n)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle", **host_cpu(),
             "sample": f"{n} of {total_rows} query rows (seeded uniform sample, all keys per row), "
                       f"fp64 C oracle, {dt:.1f} s wall"}
 
@@ -132,7 +153,7 @@ def decode_cpu_baseline(cfg, q, k, v, target_s: float):
         if dt >= target_s:
             break
     nbytes = cfg.kv_bytes() * n / total_rows * passes
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle", **host_cpu(),
             "sample": f"{passes} pass(es) over {n} of {total_rows} query rows (seeded uniform sample, "
                       f"every cached key per row), fp64 C oracle, {dt:.1f} s wall"}
 
@@ -160,7 +181,7 @@ def bwd_cpu_baseline(cfg, q, k, v, do, target_s: float):
     dt = time.perf_counter() - t0
     keys = [(int(r % cfg.N) + 1) if cfg.causal else cfg.N for r in rows]
     flops = float(sum(6 * cfg.d * kk for kk in keys))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle", **host_cpu(),
             "sample": f"dQ of {n} of {total_rows} query rows (seeded uniform sample), fp64 C oracle, "
                       f"{dt:.1f} s wall"}
 
@@ -259,7 +280,7 @@ def chunkscan_cpu_baseline(cfg, x, cb, dt, dacs, target_s: float):
     attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows, threads=threads)
     dt_s = time.perf_counter() - t0
     nbytes = cfg.hbm_bytes() * n / total_rows
-    return {"value": nbytes / dt_s / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": nbytes / dt_s / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle", **host_cpu(),
             "sample": f"{n} of {total_rows} output rows (seeded uniform sample), fp64 C oracle, {dt_s:.1f} s wall"}
 
 
@@ -384,7 +405,7 @@ def mla_bench(args):
         attn_oracle.mla_decode_rows(q, kv, cfg.Dv, cfg.scale, rows, threads=threads)
         dt_s = time.perf_counter() - t1
         cpu = {"value": cfg.hbm_bytes() * rows.size / (cfg.B * cfg.H) / dt_s / 1e9, "unit": "GB/s",
-               "cores": int(threads), "kind": "oracle",
+               "cores": int(threads), "kind": "oracle", **host_cpu(),
                "sample": f"first {rows.size} of {cfg.B * cfg.H} head rows, fp64 C oracle, {dt_s:.1f} s wall"}
     print(json.dumps({
         "metric": "MLA decode: compulsory HBM bytes per second (q and the shared latent cache read once; out, lse "

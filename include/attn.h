@@ -34,13 +34,17 @@ extern "C" {
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL_PTR = 1,   /* q, k, v, out or lse is NULL while B*H*N > 0        */
-  ATTN_ERR_BAD_SHAPE = 2,  /* B, H or N negative, or an element count overflows  */
-  ATTN_ERR_HEAD_DIM = 3,   /* d is not 64, 128 or 256                             */
-  ATTN_ERR_BAD_SCALE = 4,  /* scale is NaN, infinite or zero                      */
-  ATTN_ERR_MISALIGNED = 5, /* a pointer is not 16-byte aligned                    */
+  ATTN_ERR_BAD_SHAPE = 2,  /* B, H or N negative, an element count overflows, or
+                              (attn_fwd_variant / attn_variant_info) a variant id
+                              out of range or serving another head dimension   */
+  ATTN_ERR_HEAD_DIM = 3,   /* d is not a supported head dimension                 */
+  ATTN_ERR_BAD_SCALE = 4,  /* scale is NaN or infinite                            */
+  ATTN_ERR_MISALIGNED = 5, /* a pointer is misaligned: 16 bytes for every buffer
+                              except lse (and the backward's lse), 4 bytes       */
   ATTN_ERR_HIP = 6,        /* the HIP runtime reported an error at launch         */
-  ATTN_ERR_BAD_VARIANT = 7, /* attn_fwd_variant: id out of range or unsuited to d */
-  ATTN_ERR_WORKSPACE = 8    /* decode / backward: workspace smaller than required */
+  /* 7 is not used */
+  ATTN_ERR_WORKSPACE = 8   /* decoding, backward, MLA decoding: workspace smaller
+                              than the entry's workspace-size function reports  */
 };
 
 /*
@@ -52,9 +56,12 @@ enum attn_status {
  *   B, H, N : batch, heads, sequence length (N >= 1 any value; tails masked)
  *   d       : head dimension, one of 64, 128, 256
  *   causal  : 0 = every key visible, nonzero = key j visible to query i iff j <= i
- *   scale   : finite, nonzero float32 multiplier of q.k
+ *   scale   : finite float32 multiplier of q.k (zero and negative values
+ *             included: a zero scale gives uniform weights over the visible
+ *             keys)
  *   stream  : hipStream_t to enqueue on (NULL = the default stream)
  *
+ * Alignment: q, k, v and out 16 bytes, lse 4 bytes (else ATTN_ERR_MISALIGNED).
  * Ownership: the caller owns all five buffers; the library never allocates,
  * frees, copies or synchronises. The call is asynchronous: it enqueues the
  * kernel on `stream` and returns; device-side faults surface at the caller's
@@ -81,10 +88,11 @@ const char* attn_strerror(int status);
  *                     is out of range.
  * attn_variant_info : fills head_dim, block_m (query rows per workgroup),
  *                     block_n (keys per pipeline stage), waves per workgroup,
- *                     and lds_bytes; returns ATTN_ERR_BAD_VARIANT for a bad id.
+ *                     and lds_bytes; returns ATTN_ERR_BAD_SHAPE for a bad id.
  * attn_fwd_variant  : attn_fwd forced onto variant `id`; same arguments,
- *                     validation and semantics, plus ATTN_ERR_BAD_VARIANT when
- *                     the variant does not serve head dimension d.
+ *                     validation and semantics, plus ATTN_ERR_BAD_SHAPE when
+ *                     id is out of range or the variant does not serve head
+ *                     dimension d.
  * attn_default_variant : the variant attn_fwd picks for (d, causal), or -1.
  */
 int attn_num_variants(void);
@@ -112,7 +120,7 @@ int attn_fwd_variant(int id, const void* q, const void* k, const void* v, float*
  *   out     : device, float32, [B][H][Nq][d]; fully overwritten
  *   lse     : device, float32, [B][H][Nq];    fully overwritten
  *   Nq >= 0, Nkv >= 1 whenever B*H*Nq > 0; d one of 64, 128, 256
- *   scale   : finite, nonzero float32 multiplier of q.k
+ *   scale   : finite float32 multiplier of q.k (as for attn_fwd)
  *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
  *             aligned, at least the size attn_decode_workspace_size reports
  *             for the same shape (else ATTN_ERR_WORKSPACE); its contents on
@@ -193,8 +201,8 @@ int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_c
 
 /*
  * MLA decoding (multi-head latent attention in the absorbed form; the
- * decoding operator the PipeThreader-and-TileLang page cites as a short
- * TileLang program). Every query head of sequence b attends to one shared
+ * decoding operator the PipeThreader summary page cites in its "Discussion"
+ * paragraph, written there in about 80 lines against 500-plus by hand). Every query head of sequence b attends to one shared
  * cache of N latent rows of 576 values (512 latent + 64 rotary); a row's
  * first 512 values are its value:
  *     s_hj = scale * q_h . kv_j (576 products),  out_h = softmax_j(s_h) kv[:, 0:512],
@@ -203,7 +211,7 @@ int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_c
  *   q   : device, bf16, [B][H][576];   kv : device, bf16, [B][N][576]
  *   out : device, float32, [B][H][512]; lse : device, float32, [B][H]; fully overwritten
  *   H   : a multiple of 64 (else ATTN_ERR_BAD_SHAPE); N >= 1 when B*H > 0
- *   scale : finite, nonzero float32
+ *   scale : finite float32 (as for attn_fwd)
  *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
  *           aligned, at least mla_decode_workspace_size bytes (else
  *           ATTN_ERR_WORKSPACE); contents on entry do not matter

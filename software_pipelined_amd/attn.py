@@ -27,7 +27,6 @@ ATTN_ERR_HEAD_DIM = 3
 ATTN_ERR_BAD_SCALE = 4
 ATTN_ERR_MISALIGNED = 5
 ATTN_ERR_HIP = 6
-ATTN_ERR_BAD_VARIANT = 7
 ATTN_ERR_WORKSPACE = 8
 
 _lib = None
@@ -141,6 +140,36 @@ def attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, workspace, works
 
 # ------------------------------------------------------------ torch convenience
 
+def _check_buffer(t, name, shape, dtype, device):
+    """A caller-supplied output or workspace: a contiguous tensor of the given
+    shape and dtype on the inputs' GPU (its data pointer goes to the kernels)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, device):
+    """A workspace: contiguous and on the inputs' GPU; returns its size in
+    bytes (the C entry point reports one that is too small)."""
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
+
+
+def _used_on(stream, *tensors):
+    """Tell torch's caching allocator that the kernels enqueued on ``stream``
+    use these tensors: buffers allocated here (on the current stream) are then
+    not handed out again before that stream's work is done, even when
+    ``stream`` is not the current one."""
+    for t in tensors:
+        t.record_stream(stream)
+
+
 def attn_bwd_workspace_size(B, H, N, d):
     """(status, bytes) as returned through the C ``attn_bwd_workspace_size``."""
     n = ctypes.c_size_t(0)
@@ -176,21 +205,34 @@ def attn_backward(q, k, v, out, lse, dout, causal: bool = False, scale=None, dq=
         raise ValueError("out must be the forward's contiguous float32 [B, H, N, d] output")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be the forward's contiguous float32 [B, H, N] output")
+    for t in (k, v, dout, out, lse):
+        if t.device != q.device:
+            raise ValueError("every tensor must be on q's GPU")
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     st, need = attn_bwd_workspace_size(B, H, N, d)
     if st != ATTN_OK:
         raise AttnError(st)
-    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dq is None else dq
-    dk = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dk is None else dk
-    dv = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    made = []
+    grads = []
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+            made.append(g)
+        else:
+            _check_buffer(g, name, (B, H, N, d), torch.float32, q.device)
+        grads.append(g)
+    dq, dk, dv = grads
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
+    ws_bytes = _check_workspace(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    _used_on(stream, *made)
     st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
-                  workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+                  workspace.data_ptr(), ws_bytes, stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return dq, dk, dv
@@ -220,17 +262,31 @@ def mla_decode_torch(q, kv, scale, out=None, lse=None, workspace=None, stream=No
     N = kv.shape[1]
     if Dk != 576 or kv.shape[0] != B or kv.shape[2] != 576 or not q.is_contiguous() or not kv.is_contiguous():
         raise ValueError("q [B, H, 576] and kv [B, N, 576], contiguous")
+    if not q.is_cuda or kv.device != q.device:
+        raise ValueError("q and kv must be on one GPU")
     st, need = mla_decode_workspace_size(B, H, N)
     if st != ATTN_OK:
         raise AttnError(st)
-    out = torch.empty((B, H, 512), dtype=torch.float32, device=q.device) if out is None else out
-    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    made = []
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=q.device)
+        made.append(out)
+    else:
+        _check_buffer(out, "out", (B, H, 512), torch.float32, q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        made.append(lse)
+    else:
+        _check_buffer(lse, "lse", (B, H), torch.float32, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
+    ws_bytes = _check_workspace(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    _used_on(stream, *made)
     st = mla_decode(q.data_ptr(), kv.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, scale,
-                    workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+                    workspace.data_ptr(), ws_bytes, stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse
@@ -260,10 +316,18 @@ def mamba_chunk_scan(x, cb, dt, dA_cumsum, L: int, out=None, stream=None):
             raise ValueError("inputs must be contiguous GPU tensors")
     if dt.dtype != torch.float32 or dA_cumsum.dtype != torch.float32:
         raise ValueError("dt and dA_cumsum must be float32")
+    for t in (cb, dt, dA_cumsum):
+        if t.device != x.device:
+            raise ValueError("every tensor must be on x's GPU")
+    made = []
     if out is None:
         out = torch.empty((B, S, H, P), dtype=torch.float32, device=x.device)
+        made.append(out)
+    else:
+        _check_buffer(out, "out", (B, S, H, P), torch.float32, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
+    _used_on(stream, *made)
     st = chunk_scan(x.data_ptr(), cb.data_ptr(), dt.data_ptr(), dA_cumsum.data_ptr(), out.data_ptr(),
                     B, S, H, P, L, stream.cuda_stream)
     if st != ATTN_OK:
@@ -290,21 +354,25 @@ def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, 
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU")
     B, H, N, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    made = []
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        made.append(out)
+    else:
+        _check_buffer(out, "out", (B, H, N, d), torch.float32, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise TypeError("out and lse must be float32")
-    if tuple(out.shape) != (B, H, N, d) or tuple(lse.shape) != (B, H, N):
-        raise ValueError("out/lse shape mismatch")
-    if not (out.is_contiguous() and lse.is_contiguous()):
-        raise ValueError("out and lse must be contiguous")
+        made.append(lse)
+    else:
+        _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    _used_on(stream, *made)
     handle = stream.cuda_stream
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, H, N, d, causal, scale, handle)
@@ -332,21 +400,33 @@ def attn_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=
     Nkv = k.shape[2]
     if tuple(k.shape) != (B, H, Nkv, d) or k.shape != v.shape:
         raise ValueError("k and v must be [B, H, Nkv, d] with q's B, H and d")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU")
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     st, need = attn_decode_workspace_size(B, H, Nq, Nkv, d)
     if st != ATTN_OK:
         raise AttnError(st)
+    made = []
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        made.append(out)
+    else:
+        _check_buffer(out, "out", (B, H, Nq, d), torch.float32, q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        made.append(lse)
+    else:
+        _check_buffer(lse, "lse", (B, H, Nq), torch.float32, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
+    ws_bytes = _check_workspace(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    _used_on(stream, *made)
     st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                         B, H, Nq, Nkv, d, scale, workspace.data_ptr(), workspace.numel(),
+                         B, H, Nq, Nkv, d, scale, workspace.data_ptr(), ws_bytes,
                          stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)

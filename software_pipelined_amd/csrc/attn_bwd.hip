@@ -125,7 +125,7 @@ template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dK,
-    float* __restrict__ dV, int N, int n_ktiles, float c_log2, int negate, float scale) {
+    float* __restrict__ dV, int N, int n_ktiles, float c_log2, int q_mode, float scale) {
   constexpr int BQ = kBwdRows;
   constexpr int MAT = BQ * D * 2;
   constexpr int LD = Tile<D, NW, BQ>::LOADS;
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
   const float* st_head = stats + (size_t)bh * nqb * (2 * BQ);
 
   bf16x8 kf[1][D / 16], vf[1][D / 16];
-  load_q<D, 1>(K + head, k0w, N, negate, kf, lane);  // scale < 0: S from -K, c = |scale| log2e
+  load_q<D, 1>(K + head, k0w, N, q_mode, kf, lane);  // K as scale_args takes it
   load_q<D, 1>(V + head, k0w, N, 0, vf, lane);
   const BwdOffsets<D> bo(lane);
   f32x16 dk[D / 32], dv[D / 32];
@@ -237,7 +237,7 @@ template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dQ, int N,
-    int n_qtiles, float c_log2, int negate, float scale) {
+    int n_qtiles, float c_log2, int q_mode, float scale) {
   constexpr int MAT = BN * D * 2;
   constexpr int LD = Tile<D, NW, BN>::LOADS;
   constexpr int STAGE = 2 * MAT;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
   const int nqb = (N + kBwdRows - 1) / kBwdRows;
 
   bf16x8 qf[1][D / 16], gf[1][D / 16];
-  load_q<D, 1>(Q + head, q0w, N, negate, qf, lane);  // scale < 0: S from -Q, c = |scale| log2e
+  load_q<D, 1>(Q + head, q0w, N, q_mode, qf, lane);  // Q as scale_args takes it
   load_q<D, 1>(dO + head, q0w, N, 0, gf, lane);
   const int qs = min(qi, nqb * kBwdRows - 1);  // rows past N: padded statistics (+inf, 0)
   const float* st = stats + ((size_t)bh * nqb + qs / kBwdRows) * (2 * kBwdRows);
@@ -356,10 +356,12 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
                       const float* lse, const void* dout, float* dq, float* dk, float* dv, int N, float scale,
                       void* ws, hipStream_t stream) {
   float* stats = (float*)ws;
-  // as in the forward, a negative scale negates one operand of S exactly, so
-  // that c = |scale| log2e keeps -inf masks at -inf
-  const float c = fabsf(scale) * kLog2e;
-  const int neg = scale < 0.f;
+  // as in the forward, the sign of the scale goes into one operand of S
+  // (negated, or zeroed for a zero scale; scale_args), so that c > 0 keeps
+  // -inf masks at -inf; dK and dQ are multiplied by the scale itself
+  const ScaleArgs sa = scale_args(scale);
+  const float c = sa.c_log2;
+  const int neg = sa.q_mode;
   const unsigned gp = (unsigned)(p.bh * p.nqb);
   const unsigned gk = (unsigned)(p.bh * p.n_ktiles), gq = (unsigned)(p.bh * p.n_qtiles);
   hipLaunchKernelGGL((attn_bwd_prep<D>), dim3(gp), dim3(256), 0, stream, o, (const uint16_t*)dout, lse, stats, N,
@@ -397,7 +399,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* out, cons
   if (st != ATTN_OK) return st;
   uint32_t sbits;
   memcpy(&sbits, &scale, sizeof sbits);
-  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_BAD_SCALE;  // NaN or +-Inf
   if (p.bh == 0 || N == 0) return ATTN_OK;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_NULL_PTR;
   const uintptr_t m = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout |

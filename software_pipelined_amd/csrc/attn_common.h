@@ -322,9 +322,12 @@ __device__ __forceinline__ void mask_block(f32x16 (&s)[QT][BN / 32], int kv0, in
 //                  pb[qt][2*kb + hf] holds accumulator registers 8*hf..8*hf+7
 //                  of key tile kb;
 //   softmax_sum:   l = l * alpha + (ps0 + ps1) + (ps2 + ps3).
+//   ms_run (the overloads that take it): the running max of the unscaled
+//                  scores, which the epilogue needs to recover the dominant
+//                  key's fp32 weight (store_rows).
 template <int BN, int QT>
 __device__ __forceinline__ void softmax_stats(const f32x16 (&s)[QT][BN / 32], float c_log2,
-                                              float (&m_run)[QT], float (&alpha)[QT]) {
+                                              float (&m_run)[QT], float (&ms_run)[QT], float (&alpha)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     // four left-deep chains over the lane's 16 * BN/32 scores, written so
@@ -342,10 +345,20 @@ __device__ __forceinline__ void softmax_stats(const f32x16 (&s)[QT][BN / 32], fl
       mx[h2] = fmaxf(m, v(NV - 1));
     }
     const float bmax = swap32_max(fmaxf(fmaxf(fmaxf(mx[0], mx[1]), mx[2]), mx[3]));
+    // c > 0, so fl(max(s) c) = max(fl(s c)): m_run is the max of the scaled scores
     const float m_new = fmaxf(m_run[qt], bmax * c_log2);
     alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
     m_run[qt] = m_new;
+    ms_run[qt] = fmaxf(ms_run[qt], bmax);
   }
+}
+template <int BN, int QT>
+__device__ __forceinline__ void softmax_stats(const f32x16 (&s)[QT][BN / 32], float c_log2,
+                                              float (&m_run)[QT], float (&alpha)[QT]) {
+  float ms[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) ms[qt] = -INFINITY;
+  softmax_stats<BN, QT>(s, c_log2, m_run, ms, alpha);
 }
 
 template <int BN, int QT, int KB>
@@ -387,13 +400,22 @@ __device__ __forceinline__ void softmax_sum(float (&l_run)[QT], const float (&al
 // All of softmax for one block; S is overwritten with P (fp32).
 template <int BN, int QT>
 __device__ __forceinline__ void softmax_block(f32x16 (&s)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16],
-                                              float c_log2, float (&m_run)[QT], float (&l_run)[QT],
-                                              float (&alpha)[QT]) {
+                                              float c_log2, float (&m_run)[QT], float (&ms_run)[QT],
+                                              float (&l_run)[QT], float (&alpha)[QT]) {
   float ps[QT][4];
-  softmax_stats<BN, QT>(s, c_log2, m_run, alpha);
+  softmax_stats<BN, QT>(s, c_log2, m_run, ms_run, alpha);
   static_for<BN / 32>([&](auto KB) { softmax_exp<BN, QT, KB>(s, c_log2, m_run, ps); });
   softmax_pack<BN, QT>(s, pb);
   softmax_sum<QT>(l_run, alpha, ps);
+}
+template <int BN, int QT>
+__device__ __forceinline__ void softmax_block(f32x16 (&s)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16],
+                                              float c_log2, float (&m_run)[QT], float (&l_run)[QT],
+                                              float (&alpha)[QT]) {
+  float ms[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) ms[qt] = -INFINITY;
+  softmax_block<BN, QT>(s, pb, c_log2, m_run, ms, l_run, alpha);
 }
 
 // rescale: O *= alpha, per query tile, skipped by the whole wave when no row
@@ -438,36 +460,67 @@ __device__ __forceinline__ void pv_block(const char* Vs, const LdsOffsets<D>& of
     }
 }
 
+// How every kernel takes the scale: the exponent multiplier c = |scale| log2(e)
+// is positive (so -inf masks stay -inf and the max is taken on unscaled
+// scores), and the sign goes into the operand held in registers, q_mode:
+// 0 = as stored, 1 = every sign bit flipped (a negative scale; exact in
+// bf16), 2 = zeros (a zero scale makes every logit exactly 0, which a zero
+// operand with c = log2(e) reproduces exactly).
+struct ScaleArgs {
+  float c_log2;
+  int q_mode;
+};
+__host__ __device__ inline ScaleArgs scale_args(float scale) {
+  if (scale == 0.f) return ScaleArgs{kLog2e, 2};
+  return ScaleArgs{fabsf(scale) * kLog2e, scale < 0.f ? 1 : 0};
+}
+
+// 8 bf16 values as q_mode asks (see scale_args).
+__device__ __forceinline__ u32x4 apply_q_mode(u32x4 raw, int q_mode) {
+  if (q_mode == 1) raw ^= 0x80008000u;  // exact sign flip of 8 bf16 values
+  if (q_mode == 2) raw = u32x4{0u, 0u, 0u, 0u};
+  return raw;
+}
+
 // Load the wave's Q^T fragments (B operand of mma_qk): lane holds
-// Q[q][kk*16 + h*8 .. +7] for its query q of each tile (rows past N clamped).
+// Q[q][kk*16 + h*8 .. +7] for its query q of each tile (rows past N clamped),
+// taken as q_mode asks.
 template <int D, int QT>
-__device__ __forceinline__ void load_q(const uint16_t* Qh, int q0w, int N, int negate_q,
+__device__ __forceinline__ void load_q(const uint16_t* Qh, int q0w, int N, int q_mode,
                                        bf16x8 (&qf)[QT][D / 16], int lane) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qrow = min(q0w + 32 * qt + (lane & 31), N - 1);
     const uint16_t* qp = Qh + (size_t)qrow * D + (lane >> 5) * 8;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 raw = *(const u32x4*)(qp + kk * 16);
-      if (negate_q) raw ^= 0x80008000u;  // exact sign flip of 8 bf16 values
-      qf[qt][kk] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[qt][kk] = __builtin_bit_cast(bf16x8, apply_q_mode(*(const u32x4*)(qp + kk * 16), q_mode));
   }
 }
 
 // Epilogue: O = O_acc / l and LSE = ln2 * (m + log2 l), stored for rows < N.
-template <int D, int QT>
-__device__ __forceinline__ void store_rows(float* O, float* LSE, size_t head, size_t bh, int N,
-                                           int qi0, const f32x16 (&o)[QT][D / 32],
-                                           const float (&m_run)[QT], const float (&l_run)[QT],
-                                           int lane) {
+// With ms_run (the unscaled running max) O is normalised by l with the
+// dominant key's weight taken as the matrix core used it: that weight is
+// exp2 of the exponent argument's fp32 residual fma(s_max, c, -fl(s_max c)),
+// within 2^-19 of 1 in fp32 (what l holds) and exactly 1 in bf16 (what O_acc
+// holds). So a row whose softmax is one-hot up to fp32 (causal row 0, a key
+// far above the others) stores exactly its dominant V row. LSE uses l.
+template <int D, int QT, bool DOM>
+__device__ __forceinline__ void store_rows_impl(float* O, float* LSE, size_t head, size_t bh, int N,
+                                                int qi0, const f32x16 (&o)[QT][D / 32],
+                                                const float (&m_run)[QT], const float (&ms_run)[QT],
+                                                const float (&l_run)[QT], float c_log2, int lane) {
   const int h = lane >> 5;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qi = qi0 + 32 * qt;
     const float l_tot = swap32_sum(l_run[qt]);
-    const float inv = 1.0f / l_tot;
+    float l_o = l_tot;
+    if constexpr (DOM) {
+      const float p_dom = __builtin_amdgcn_exp2f(__builtin_fmaf(ms_run[qt], c_log2, -m_run[qt]));
+      l_o = (l_tot - p_dom) + 1.0f;
+    }
+    const float inv = 1.0f / l_o;
     if (qi < N) {
       float* orow = O + head + (size_t)qi * D;
 #pragma unroll
@@ -481,6 +534,19 @@ __device__ __forceinline__ void store_rows(float* O, float* LSE, size_t head, si
       if (h == 0) LSE[bh * N + qi] = kLn2 * (m_run[qt] + __builtin_amdgcn_logf(l_tot));
     }
   }
+}
+template <int D, int QT>
+__device__ __forceinline__ void store_rows(float* O, float* LSE, size_t head, size_t bh, int N, int qi0,
+                                           const f32x16 (&o)[QT][D / 32], const float (&m_run)[QT],
+                                           const float (&ms_run)[QT], const float (&l_run)[QT], float c_log2,
+                                           int lane) {
+  store_rows_impl<D, QT, true>(O, LSE, head, bh, N, qi0, o, m_run, ms_run, l_run, c_log2, lane);
+}
+template <int D, int QT>
+__device__ __forceinline__ void store_rows(float* O, float* LSE, size_t head, size_t bh, int N, int qi0,
+                                           const f32x16 (&o)[QT][D / 32], const float (&m_run)[QT],
+                                           const float (&l_run)[QT], int lane) {
+  store_rows_impl<D, QT, false>(O, LSE, head, bh, N, qi0, o, m_run, m_run, l_run, 0.f, lane);
 }
 
 // Everything a block step needs besides the per-block registers.

@@ -46,7 +46,7 @@ template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int BH, int Nq, int Nkv, int n_qt, int nc,
-    float c_log2, int negate_q) {
+    float c_log2, int q_mode) {
   constexpr int ST = 2;
   constexpr int MAT = BN * D * 2;
   constexpr int PER_BLOCK = 2 * Tile<D, 1, BN>::LOADS;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
   auto vs = [ring](int s) { return ring + (ST + s) * MAT; };
 
   bf16x8 qf[1][D / 16];
-  load_q<D, 1>(Q + (size_t)bh * Nq * D, qt0, Nq, negate_q, qf, lane);
+  load_q<D, 1>(Q + (size_t)bh * Nq * D, qt0, Nq, q_mode, qf, lane);
   if constexpr (NW <= 4) park_in_agprs<1, D / 16>(qf);
   const LdsOffsets<D> off(lane);
   f32x16 o[1][D / 32];
@@ -240,8 +240,9 @@ int decode_plan(int B, int H, int Nq, int Nkv, int d, DecodePlan* p) {
 template <int D, int NW>
 hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, const void* v, float* out,
                          float* lse, int BH, int Nq, int Nkv, float scale, void* ws, hipStream_t stream) {
-  const float c = fabsf(scale) * kLog2e;
-  const int neg = scale < 0.f;
+  const ScaleArgs sa = scale_args(scale);
+  const float c = sa.c_log2;
+  const int neg = sa.q_mode;
   float* ws_o = (float*)ws;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * D;
   const dim3 grid((unsigned)(BH * p.n_qt), (unsigned)(p.nc / NW)), block(NW * 64);
@@ -252,6 +253,28 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
   hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)rows), dim3(256), 0, stream,
                      (const float*)ws_o, (const float*)ws_lse, out, lse, rows, p.nc);
   return hipGetLastError();
+}
+
+// Argument checks of the decoding entry (before any HIP call).
+int decode_check(const DecodePlan& p, const void* q, const void* k, const void* v, const float* out,
+                 const float* lse, float scale) {
+  uint32_t sbits;
+  memcpy(&sbits, &scale, sizeof sbits);
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_BAD_SCALE;  // NaN or +-Inf
+  if (p.rows == 0) return ATTN_OK;
+  if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_PTR;
+  const uintptr_t m = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
+  if ((m & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
+}
+
+hipError_t launch_decode_d(int d, const DecodePlan& p, const void* q, const void* k, const void* v, float* out,
+                           float* lse, int BH, int Nq, int Nkv, float scale, void* ws, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_decode<64, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
+    case 128: return launch_decode<128, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
+    default: return launch_decode<256, 2>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
+  }
 }
 
 }  // namespace
@@ -271,21 +294,13 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, flo
   DecodePlan p;
   int st = decode_plan(B, H, Nq, Nkv, d, &p);
   if (st != ATTN_OK) return st;
-  uint32_t sbits;
-  memcpy(&sbits, &scale, sizeof sbits);
-  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
-  if (p.rows == 0) return ATTN_OK;
-  if (!q || !k || !v || !out || !lse || !workspace) return ATTN_ERR_NULL_PTR;
-  const uintptr_t m = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)workspace;
-  if ((m & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_MISALIGNED;
+  st = decode_check(p, q, k, v, out, lse, scale);
+  if (st != ATTN_OK || p.rows == 0) return st;
+  if (!workspace) return ATTN_ERR_NULL_PTR;
+  if (((uintptr_t)workspace & 15) != 0) return ATTN_ERR_MISALIGNED;
   if (workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
-  const int BH = B * H;
-  hipError_t e;
-  switch (d) {
-    case 64: e = launch_decode<64, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
-    case 128: e = launch_decode<128, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
-    default: e = launch_decode<256, 2>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, workspace, (hipStream_t)stream); break;
-  }
+  const hipError_t e = launch_decode_d(d, p, q, k, v, out, lse, B * H, Nq, Nkv, scale, workspace,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -1,5 +1,6 @@
 // Fused attention forward for MI355X (gfx950, CDNA4), behind the C ABI in
-// include/attn.h.
+// include/attn.h: the C entry points. The kernels are in attn_fwd_kernels.h,
+// the variant tables in attn_fwd_d64.hip, attn_fwd_d128.hip, attn_fwd_d256.hip.
 //
 // What is computed (PipeThreader, OSDI'25 summary page, "FlashAttention-3"
 // paragraph and Fig 7; "PipeThreader and TileLang" page, section 4.1): per
@@ -40,634 +41,47 @@
 // turns on the matrix core) and "pipe" (each wave overlaps the softmax of
 // block j with the QK^T MFMAs of block j+1).
 
-#include "attn_common.h"
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn.h"
+#include "attn_fwd_variants.h"
 
 namespace {
 
-// ---------------------------------------------------------------- simple kernel
-// Blocks stream through an ST-slot ring (block j in slot j mod ST): at the
-// top of block j every wave waits for its share of block j's copies, meets
-// the others at the barrier (so slot (j-1) mod ST is no longer read), and
-// starts the copies of block j+ST-1 into that slot; then the steps of block j
-// run in program order. The reference schedule the overlapped kernels are
-// checked against (bit for bit).
-template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int SLOT>
-__device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
-                                             const LdsOffsets<D>& off,
-                                             const bf16x8 (&qf)[QT][D / 16],
-                                             f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
-                                             float (&l_run)[QT]) {
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
-  constexpr int PER_BLOCK = 2 * LD;  // copy instructions per block per wave
-  // every block issues its copies (past the last block a clamped duplicate
-  // lands in a free slot), so the count of younger copies is always exact
-  wait_vmcnt<(ST - 2) * PER_BLOCK>();  // blocks j+1 .. j+ST-2 may stay in flight
-  block_barrier();
-  constexpr int NS = (SLOT + ST - 1) % ST;
-  const int row_next = min(j + ST - 1, c.nblk - 1) * BN;
-  const int kv0 = j * BN;
-  if (kv0 >= c.kv_end_w) {  // wave-uniform: the whole block is masked for this wave
-#pragma unroll
-    for (int t = 0; t < LD; ++t) {
-      issue_copy<D, NW, BN, false>(c.Kh, row_next, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
-      issue_copy<D, NW, BN, true>(c.Vh, row_next, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
-    }
-    return;
-  }
-  // copies of block j+ST-1 interleaved with the mma_qk stream of block j
-  f32x16 s[QT][BN / 32];
-  qk_block_with_copies<D, BN, QT, PER_BLOCK>(k_slot<D, BN, ST>(smem, SLOT), off, qf, s, [&](int ci) {
-    const int t = ci >> 1;
-    if (ci & 1)
-      issue_copy<D, NW, BN, true>(c.Vh, row_next, c.N, v_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
-    else
-      issue_copy<D, NW, BN, false>(c.Kh, row_next, c.N, k_slot<D, BN, ST>(smem, NS), c.wave, c.lane, t);
-  });
-  sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
-  if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
-  bf16x8 pb[QT][BN / 16];
-  float alpha[QT];
-  softmax_block<BN, QT>(s, pb, c.c_log2, m_run, l_run, alpha);
-  rescale_block<D, QT>(o, alpha);
-  pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, SLOT), off, pb, o);
-  sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
-}
+using attn_fwd_impl::Variant;
 
-// OCC = workgroups per CU the register budget is sized for (waves per SIMD =
-// NW * OCC / 4): with NW = 4 and OCC = 2 two independent workgroups share a
-// CU, so the two waves on each SIMD are never held in step by one barrier.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int OCC>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
-    int n_qtiles, float c_log2, int negate_q) {
-  using T = Tile<D, NW, BN, QT, ST>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
-
-  // Q first, then blocks 0 .. ST-2 (so the in-loop waits count block copies only)
-  bf16x8 qf[QT][D / 16];
-  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
-  if constexpr (NW * OCC <= 4) park_in_agprs<QT, D / 16>(qf);
-#pragma unroll
-  for (int b = 0; b < ST - 1; ++b)
-    if (b < c.nblk) {
-      issue_block_load<D, NW, BN, false>(c.Kh, b * BN, N, k_slot<D, BN, ST>(smem, b), c.wave, c.lane);
-      issue_block_load<D, NW, BN, true>(c.Vh, b * BN, N, v_slot<D, BN, ST>(smem, b), c.wave, c.lane);
-    }
-  const LdsOffsets<D> off(c.lane);
-  f32x16 o[QT][D / 32];
-  float m_run[QT], l_run[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-  }
-  for (int j = 0; j < c.nblk; j += ST) {
-    simple_block<D, NW, BN, QT, CAUSAL, ST, 0>(c, smem, j, off, qf, o, m_run, l_run);
-    if (j + 1 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 1 % ST>(c, smem, j + 1, off, qf, o, m_run, l_run);
-    if (ST > 2 && j + 2 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 2 % ST>(c, smem, j + 2, off, qf, o, m_run, l_run);
-    if (ST > 3 && j + 3 < c.nblk) simple_block<D, NW, BN, QT, CAUSAL, ST, 3 % ST>(c, smem, j + 3, off, qf, o, m_run, l_run);
-  }
-  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
-  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
-}
-
-// ---------------------------------------------------------------- pipelined kernel
-// Software-pipelined schedule inside each wave (the pages' FlashAttention-
-// forward schedule found by Twill, section 3.1 of the software-pipelining
-// page: the first GEMM is hoisted into the loop prologue so exp latency is
-// never exposed, and one tile's softmax overlaps the other GEMMs), restated
-// for gfx950. A wave's MFMAs run alongside its own VALU work, so every phase
-// gives the wave both kinds of work:
-//   prologue : K_0 .. K_{ST-1}, V_0 .. V_{ST-3} -> LDS; S_0 = Q K_0^T
-//   block j  : (a) mma_pv(V_{j-1}, P_{j-1})  with  mask, row max and the
-//                  first half of the exp units of S_j;
-//              (b) mma_qk(K_{j+1}) -> S_{j+1}  with  the other exp units,
-//                  row sums and packing of P_j;
-//              then O *= alpha_j per query tile (skipped for a tile when no
-//              row of it moved its max)
-//   epilogue : mma_pv(V_{n-1}, P_{n-1})
-// An exp unit is one (query tile, 32-key tile) pair, taken query-tile-major,
-// so with one key tile and two query tiles each phase gets one tile's exps.
-// O sees exactly the simple schedule's sequence of updates (... += P_{j-1}V,
-// *= alpha_j, += P_j V ...), so results agree bit for bit. LDS holds ST K
-// and ST V slots (K_i and V_i in slot i mod ST). At the top of block j each
-// wave waits for its copies of K_{j+1} and V_{j-1} (those of the last ST-2
-// blocks may stay in flight), meets the others at the barrier (after which
-// K_j and V_{j-2} are no longer read) and, spread through phase (b), copies
-// K_{j+ST} over K_j and V_{j+ST-2} over V_{j-2}: ST-1 blocks of latency.
-
-// MFMA stream of NR read groups (RD reads each, feeding MR MFMAs) with NV
-// VALU instructions after every MFMA and NVM VMEM copies spread over the
-// steady part; reads run PF groups ahead.
-template <int I, int NR, int PF, int RD, int MR, int NV, int NVM>
-__device__ __forceinline__ void sched_valu_steps() {
-  if constexpr (I < NR - PF) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-    constexpr int due = copies_due<NR, PF, NVM>(I);
-    if constexpr (due > 0) __builtin_amdgcn_sched_group_barrier(0x010, due, 0);
-    sched_valu_steps<I + 1, NR, PF, RD, MR, NV, NVM>();
-  }
-}
-template <int NR, int RD, int MR, int PF, int NV, int NVM>
-__device__ __forceinline__ void sched_mfma_reads_valu_copies() {
-  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, 0);
-  sched_valu_steps<0, NR, PF, RD, MR, NV, NVM>();
-#pragma unroll
-  for (int i = 0; i < PF * MR; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-  }
-}
-
-template <int D, int NW, int BN, int ST, int SLOT>
-__device__ __forceinline__ auto pipe_top(const Ctx& c, char* smem, int j) {
-  constexpr int PER_BLOCK = 2 * Tile<D, NW, BN>::LOADS;  // copies per block per wave
-  wait_vmcnt<(ST - 2) * PER_BLOCK>();
-  block_barrier();
-  // past the last block a clamped duplicate lands in a slot nobody reads again
-  const int row_k = min(j + ST, c.nblk - 1) * BN;
-  const int row_v = min(j + ST - 2, c.nblk - 1) * BN;
-  return [&c, smem, row_k, row_v](int ci) {
-    const int t = ci >> 1;
-    if (ci & 1)
-      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, ST>(smem, (SLOT + ST - 2) % ST), c.wave,
-                                  c.lane, t);
-    else
-      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, ST>(smem, SLOT), c.wave, c.lane, t);
-  };
-}
-
-// Exp units [U0, U1) of S (unit u = query tile u / NB, key tile u % NB).
-template <int BN, int QT, int U0, int U1>
-__device__ __forceinline__ void softmax_exp_units(f32x16 (&s)[QT][BN / 32], float c_log2,
-                                                  const float (&m_run)[QT], float (&ps)[QT][4]) {
-  constexpr int NB = BN / 32;
-  static_for_from<U0, U1>([&](auto U) {
-    constexpr int qt = U / NB, kb = U % NB;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kb][r], c_log2, -m_run[qt]));
-      s[qt][kb][r] = p;
-      if (kb == 0 && r < 4) ps[qt][r] = p;
-      else ps[qt][r & 3] += p;
-    }
-  });
-}
-
-// Block j when the whole workgroup has P_{j-1}, an unmasked S_j and a next
-// block: both phases overlapped.
-template <int D, int NW, int BN, int QT, int ST, int SLOT>
-__device__ __forceinline__ void pipe_block_fast(const Ctx& c, char* smem, int j, const LdsOffsets<D>& off,
-                                                const bf16x8 (&qf)[QT][D / 16],
-                                                f32x16 (&s_cur)[QT][BN / 32],
-                                                f32x16 (&s_nxt)[QT][BN / 32], bf16x8 (&pb)[QT][BN / 16],
-                                                f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
-                                                float (&l_run)[QT]) {
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
-  constexpr int NB = BN / 32;
-  constexpr int NU = QT * NB, UA = (NU + 1) / 2;  // exp units, and those of phase (a)
-  constexpr int MA = (BN / 16) * (D / 32) * QT, MB = (D / 16) * NB * QT;  // MFMAs per phase
-  // VALU instructions placed after each MFMA: with one query tile the tuned
-  // 5 and 4; else about the phase's count (an exp unit is 16 fma, exp and
-  // add; stats take 8 max3 per key tile plus 6; packing and the sums 8 per
-  // key tile plus 4 per query tile) over its MFMAs
-  constexpr int NVA = QT == 1 ? 5 : (QT * (8 * NB + 6) + UA * 48 + MA - 1) / MA;
-  constexpr int NVB = QT == 1 ? 4 : ((NU - UA) * 48 + QT * (8 * NB + 4) + MB - 1) / MB;
-  auto copy = pipe_top<D, NW, BN, ST, SLOT>(c, smem, j);
-  float alpha[QT], ps[QT][4];
-  // (a) mma_pv(V_{j-1}) with the row maxima and the first exp units
-  pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, (SLOT + ST - 1) % ST), off, pb, o);
-  softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
-  softmax_exp_units<BN, QT, 0, UA>(s_cur, c.c_log2, m_run, ps);
-  static_for<UA>([&](auto U) {
-    pin(s_cur[U / NB][U % NB]);
-    if constexpr (U % NB == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pin(ps[U / NB][e]);
-    }
-  });
-  sched_mfma_reads_valu_copies<(BN / 16) * (D / 32), 2, QT, kPfPV, NVA, 0>();
-  __builtin_amdgcn_sched_barrier(0);
-  // (b) mma_qk(K_{j+1}) with this block's copies, the remaining exp units, row
-  // sums and packing. (Copies sit among the K reads: plain LDS loads whose
-  // addresses the compiler can tell apart from the copy destinations; next to
-  // the transposing V reads it would wait for every copy to land.)
-  qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, ST>(smem, (SLOT + 1) % ST), off, qf, s_nxt, copy);
-  softmax_exp_units<BN, QT, UA, NU>(s_cur, c.c_log2, m_run, ps);
-  softmax_sum<QT>(l_run, alpha, ps);
-  softmax_pack<BN, QT>(s_cur, pb);
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    pin(l_run[qt]);
-#pragma unroll
-    for (int p = 0; p < BN / 16; ++p) pin(pb[qt][p]);
-  }
-  sched_mfma_reads_valu_copies<(D / 16) * NB, 1, QT, kPfQK, NVB, 2 * LD>();
-  __builtin_amdgcn_sched_barrier(0);
-  rescale_block<D, QT>(o, alpha);
-}
-
-// Any block (first, masked, past a wave's causal limit, last): the same
-// steps in the same order, without overlap.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int SLOT>
-__device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int j,
-                                                   const LdsOffsets<D>& off,
-                                                   const bf16x8 (&qf)[QT][D / 16],
-                                                   f32x16 (&s_cur)[QT][BN / 32],
-                                                   f32x16 (&s_nxt)[QT][BN / 32],
-                                                   bf16x8 (&pb)[QT][BN / 16], f32x16 (&o)[QT][D / 32],
-                                                   float (&m_run)[QT], float (&l_run)[QT]) {
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
-  constexpr int NB = BN / 32;
-  auto copy = pipe_top<D, NW, BN, ST, SLOT>(c, smem, j);
-#pragma unroll
-  for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
-  const int kv0 = j * BN;
-  const bool act = kv0 < c.kv_end_w;                         // S_j has live keys (wave-uniform)
-  const bool prv = j > 0 && kv0 - BN < c.kv_end_w;           // P_{j-1} exists
-  const bool nxt = j + 1 < c.nblk && kv0 + BN < c.kv_end_w;  // S_{j+1} is needed
-  float alpha[QT], ps[QT][4];
-  if (prv) {
-    pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, (SLOT + ST - 1) % ST), off, pb, o);
-    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPV>();
-  }
-  if (act) {
-    if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s_cur, kv0, c.qi0, c.N, c.lane);
-    softmax_stats<BN, QT>(s_cur, c.c_log2, m_run, alpha);
-    softmax_exp_units<BN, QT, 0, (QT * NB + 1) / 2>(s_cur, c.c_log2, m_run, ps);
-  }
-  if (nxt) {
-    qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, (SLOT + 1) % ST), off, qf, s_nxt);
-    sched_mfma_with_reads<(D / 16) * NB, 1, QT, kPfQK>();
-  }
-  if (act) {
-    softmax_exp_units<BN, QT, (QT * NB + 1) / 2, QT * NB>(s_cur, c.c_log2, m_run, ps);
-    softmax_sum<QT>(l_run, alpha, ps);
-    softmax_pack<BN, QT>(s_cur, pb);
-    rescale_block<D, QT>(o, alpha);
-  }
-}
-
-// NW waves, QT query tiles of 32 per wave, BN keys per block, ST ring slots
-// (even: the S buffers swap roles every block).
-template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int ST>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipelined(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
-    int n_qtiles, float c_log2, int negate_q) {
-  static_assert(ST % 2 == 0, "the block loop is unrolled by ST and S alternates by parity");
-  using T = Tile<D, NW, BN, QT, ST>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
-
-  // prologue: Q; K_0 .. K_{ST-1} and V_0 .. V_{ST-3} in flight; S_0 = Q K_0^T
-  bf16x8 qf[QT][D / 16];
-  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
-  if constexpr (NW * OCC <= 4) park_in_agprs<QT, D / 16>(qf);
-  static_for<ST>([&](auto I) {
-    if (I < c.nblk) {
-      issue_block_load<D, NW, BN, false>(c.Kh, I * BN, N, k_slot<D, BN, ST>(smem, I), c.wave, c.lane);
-      if constexpr (I + 2 < ST)
-        issue_block_load<D, NW, BN, true>(c.Vh, I * BN, N, v_slot<D, BN, ST>(smem, I), c.wave, c.lane);
-    }
-  });
-  const LdsOffsets<D> off(c.lane);
-  f32x16 o[QT][D / 32];
-  float m_run[QT], l_run[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-  }
-  f32x16 sa[QT][BN / 32], sb[QT][BN / 32];
-  bf16x8 pb[QT][BN / 16];
-  wait_vmcnt<0>();
-  block_barrier();
-  qk_block<D, BN, QT>(k_slot<D, BN, ST>(smem, 0), off, qf, sa);  // block 0 is never skipped
-  sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
-
-  // Blocks 1 .. jf-1 take the overlapped path for every wave: they have a
-  // previous and a next block, no key past N and (causal) no key past the
-  // workgroup's first query. Block 0 and blocks jf .. n-1 take the generic
-  // path. Block j uses slot j mod ST; S roles alternate with its parity.
-  const int n = c.nblk;
-  int jf = n - 1;
-  if (N % BN) jf = min(jf, N / BN);
-  if (CAUSAL) jf = min(jf, (c.q0 + 1) / BN);
-  pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, 0>(c, smem, 0, off, qf, sa, sb, pb, o, m_run, l_run);
-  int j = 1;
-  for (; j + ST - 1 < jf; j += ST) {
-    static_for<ST>([&](auto I) {
-      constexpr int slot = (1 + I) % ST;
-      if constexpr ((1 + I) % 2)
-        pipe_block_fast<D, NW, BN, QT, ST, slot>(c, smem, j + I, off, qf, sb, sa, pb, o, m_run, l_run);
-      else
-        pipe_block_fast<D, NW, BN, QT, ST, slot>(c, smem, j + I, off, qf, sa, sb, pb, o, m_run, l_run);
-    });
-  }
-  for (; j < n; j += ST) {
-    static_for<ST>([&](auto I) {
-      constexpr int slot = (1 + I) % ST;
-      if (j + I < n) {
-        if constexpr ((1 + I) % 2)
-          pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, slot>(c, smem, j + I, off, qf, sb, sa, pb, o, m_run, l_run);
-        else
-          pipe_block_generic<D, NW, BN, QT, CAUSAL, ST, slot>(c, smem, j + I, off, qf, sa, sb, pb, o, m_run, l_run);
-      }
-    });
-  }
-  // epilogue: mma_pv of the last block (V_{n-1} in slot (n-1) mod ST)
-  wait_vmcnt<0>();
-  block_barrier();
-  if ((n - 1) * BN < c.kv_end_w) {
-    static_for<ST>([&](auto I) {
-      if ((n - 1) % ST == I) pv_block<D, BN, QT>(v_slot<D, BN, ST>(smem, I), off, pb, o);
-    });
-  }
-  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
-}
-
-// ---------------------------------------------------------------- ping-pong kernel
-// Two wave groups per workgroup (A = waves 0..NW/2-1, B = the rest; each
-// SIMD holds one wave of each) alternate on the matrix core, half a block
-// apart -- the pages' forward schedule in which two compute groups take turns
-// on the matrix unit while the other runs the softmax (software-pipelining
-// page, section 3.1), restated for gfx950 with s_barrier as the turn signal.
-// Intervals t = 0, 1, ..., 2n (n = KV blocks) are separated by barriers:
-//
-//   interval   group A                   group B
-//   prologue   S_0 = Q K_0^T              -
-//   2j         softmax_j (+rescale)       mma_pv(V_{j-1}), S_j = Q K_j^T
-//   2j+1       mma_pv(V_j), S_{j+1}       softmax_j (+rescale)
-//
-// K_j is read in intervals 2j-1 (A) and 2j (B), V_j in 2j+1 (A) and 2j+2
-// (B); at barrier 2m+1 the copies of K_{m+2} (over K_m) and V_{m+1} (over
-// V_{m-1}) start, and each wave waits for them before barrier 2m+3. Each
-// group runs its own loop; both pass the same number of barriers.
-template <int D, int NW, int BN, int QT, bool CAUSAL, int VS, int KS, typename CopyFn>
-__device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int jp,
-                                                   const LdsOffsets<D>& off,
-                                                   const bf16x8 (&qf)[QT][D / 16],
-                                                   f32x16 (&s)[QT][BN / 32],
-                                                   const bf16x8 (&pb)[QT][BN / 16],
-                                                   f32x16 (&o)[QT][D / 32], int ncopy, CopyFn&& copy) {
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
-  // the wave on the matrix core issues ahead of the wave in its softmax turn
-  // (measured: +2% over equal priority, -2% with the priorities reversed)
-  __builtin_amdgcn_s_setprio(1);
-  if (jp >= 0 && jp < c.nblk && jp * BN < c.kv_end_w) {
-    pv_block<D, BN, QT>(v_slot<D, BN, 2>(smem, VS), off, pb, o);
-    sched_mfma_with_reads<(BN / 16) * (D / 32), 2, QT, kPfPVTurn>();
-  }
-  const int jq = jp + 1;
-  if (jq < c.nblk && jq * BN < c.kv_end_w) {
-    if (ncopy)
-      qk_block_with_copies<D, BN, QT, 2 * LD>(k_slot<D, BN, 2>(smem, KS), off, qf, s, copy);
-    else
-      qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, KS), off, qf, s);
-    sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
-  } else if (ncopy) {
-#pragma unroll
-    for (int ci = 0; ci < 2 * LD; ++ci) copy(ci);
-  }
-}
-
-// The softmax turn, with NCOPY copy instructions (group B's share of the
-// next blocks): half open the turn, half follow the row sums, where the
-// texture path has drained the other group's copies (measured +1% over all
-// at the start; one after each key tile's exps measured no better).
-template <int D, int BN, int QT, bool CAUSAL, int NCOPY, typename CopyFn>
-__device__ __forceinline__ void pingpong_valu_turn(const Ctx& c, int j, f32x16 (&s)[QT][BN / 32],
-                                                   bf16x8 (&pb)[QT][BN / 16],
-                                                   f32x16 (&o)[QT][D / 32], float (&m_run)[QT],
-                                                   float (&l_run)[QT], CopyFn&& copy) {
-  constexpr int NB = BN / 32;
-  __builtin_amdgcn_s_setprio(0);
-  if (j < c.nblk && j * BN < c.kv_end_w) {
-    const int kv0 = j * BN;
-#pragma unroll
-    for (int ci = 0; ci < NCOPY / 2; ++ci) copy(ci);
-    if (block_needs_mask<BN, CAUSAL>(c, kv0)) mask_block<BN, QT, CAUSAL>(s, kv0, c.qi0, c.N, c.lane);
-    float alpha[QT], ps[QT][4];
-    softmax_stats<BN, QT>(s, c.c_log2, m_run, alpha);
-    static_for<NB>([&](auto KB) { softmax_exp<BN, QT, KB>(s, c.c_log2, m_run, ps); });
-    softmax_pack<BN, QT>(s, pb);
-    softmax_sum<QT>(l_run, alpha, ps);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ci = NCOPY / 2; ci < NCOPY; ++ci) copy(ci);
-    __builtin_amdgcn_sched_barrier(0);
-    rescale_block<D, QT>(o, alpha);
-  } else {
-#pragma unroll
-    for (int ci = 0; ci < NCOPY; ++ci) copy(ci);
-  }
-}
-
-// Start of an odd interval t = 2m+1: every wave waits for its share of the
-// copies started two intervals ago and meets the others at the barrier; the
-// copies of K_{m+2} (over K_m, slot MS) and V_{m+1} (over V_{m-1}, slot MS^1)
-// are then issued by the returned functor, spread over the wave's next turn.
-// Past the last block a clamped duplicate lands in a slot nobody reads again.
-template <int D, int NW, int BN, int MS>
-__device__ __forceinline__ auto pingpong_odd_barrier(const Ctx& c, char* smem, int m) {
-  wait_vmcnt<0>();
-  block_barrier();
-  const int row_k = min(m + 2, c.nblk - 1) * BN;
-  const int row_v = min(m + 1, c.nblk - 1) * BN;
-  return [&c, smem, row_k, row_v](int ci) {
-    const int t = ci >> 1;
-    if (ci & 1)
-      issue_copy<D, NW, BN, true>(c.Vh, row_v, c.N, v_slot<D, BN, 2>(smem, MS ^ 1), c.wave, c.lane, t);
-    else
-      issue_copy<D, NW, BN, false>(c.Kh, row_k, c.N, k_slot<D, BN, 2>(smem, MS), c.wave, c.lane, t);
-  };
-}
-
-template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
-    int n_qtiles, float c_log2, int negate_q) {
-  using T = Tile<D, NW, BN, QT, 2>;
-  static_assert(NW % 2 == 0, "two wave groups");
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
-
-  bf16x8 qf[QT][D / 16];
-  load_q<D, QT>(Q + c.head, c.q0w, N, negate_q, qf, c.lane);
-  issue_block_load<D, NW, BN, false>(c.Kh, 0, N, k_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
-  issue_block_load<D, NW, BN, true>(c.Vh, 0, N, v_slot<D, BN, 2>(smem, 0), c.wave, c.lane);
-  if (c.nblk > 1)
-    issue_block_load<D, NW, BN, false>(c.Kh, BN, N, k_slot<D, BN, 2>(smem, 1), c.wave, c.lane);
-  const LdsOffsets<D> off(c.lane);
-  f32x16 o[QT][D / 32];
-  float m_run[QT], l_run[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) o[qt][t] = f32x16{};
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-  }
-  f32x16 s[QT][BN / 32];
-  bf16x8 pb[QT][BN / 16];
-  wait_vmcnt<0>();
-  block_barrier();
-  const int n = c.nblk;
-  constexpr int LD = Tile<D, NW, BN>::LOADS;
-  auto no_copy = [](int) {};
-  // Both groups pass 2n+1 barriers after the prologue one.
-  if (c.wave < NW / 2) {
-    qk_block<D, BN, QT>(k_slot<D, BN, 2>(smem, 0), off, qf, s);  // S_0 (block 0 is never skipped)
-    sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
-    for (int j = 0; j < n; j += 2) {
-      // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
-      block_barrier();
-      pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j, s, pb, o, m_run, l_run, no_copy);
-      {
-        auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
-        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 1, copy);
-      }
-      if (j + 1 < n) {  // block j+1 (odd): slots swap
-        block_barrier();
-        pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j + 1, s, pb, o, m_run, l_run, no_copy);
-        auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
-        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o, 1, copy);
-      }
-    }
-    block_barrier();  // t = 2n: group B's last mma_pv
-  } else {
-    for (int j = 0; j < n; j += 2) {
-      // block j (even): [t=2j] pv(j-1) from V slot 1, qk(j) from K slot 0 | [t=2j+1] softmax
-      block_barrier();
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o, 0, no_copy);
-      {
-        auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
-        pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j, s, pb, o, m_run, l_run, copy);
-      }
-      if (j + 1 < n) {
-        block_barrier();
-        pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 0, no_copy);
-        auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
-        pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j + 1, s, pb, o, m_run, l_run, copy);
-      }
-    }
-    block_barrier();  // t = 2n: mma_pv of the last block, from V slot (n-1) & 1
-    if (n & 1)
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, n - 1, off, qf, s, pb, o, 0, no_copy);
-    else
-      pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, n - 1, off, qf, s, pb, o, 0, no_copy);
-  }
-  wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
-  store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, l_run, c.lane);
-}
-
-// ---------------------------------------------------------------- host side
-
-typedef hipError_t (*launch_fn)(const void*, const void*, const void*, float*, float*, int, int,
-                                int, int, float, hipStream_t);
-
-enum Schedule { kSimple = 0, kPipelined = 1, kPingPong = 2 };
-
-template <int D, int NW, int BN, int QT, int SCHED, int ST, int OCC = 1>
-hipError_t launch(const void* q, const void* k, const void* v, float* out, float* lse, int B,
-                  int H, int N, int causal, float scale, hipStream_t stream) {
-  using T = Tile<D, NW, BN, QT, ST>;
-  const int n_qt = (N + T::BM - 1) / T::BM;
-  const long long G = (long long)B * H * n_qt;
-  const float c = fabsf(scale) * kLog2e;
-  const int neg = scale < 0.f;
-  const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
-  const dim3 grid((unsigned)G), block(NW * 64);
-  if constexpr (SCHED == kPingPong) {
-    if (causal)
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-    else
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-  } else if constexpr (SCHED == kPipelined) {
-    if (causal)
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, true, OCC, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-    else
-      hipLaunchKernelGGL((attn_fwd_pipelined<D, NW, BN, QT, false, OCC, ST>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-  } else {
-    if (causal)
-      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, true, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-    else
-      hipLaunchKernelGGL((attn_fwd_simple<D, NW, BN, QT, false, ST, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
-  }
-  return hipGetLastError();
-}
-
-struct Variant {
-  const char* name;
-  int d, bm, bn, waves, lds;
-  launch_fn fn;
+// Variant ids run through the d = 64, 128 and 256 tables in that order.
+struct Table {
+  const Variant* v;
+  int n;
 };
-
-#define VARIANT(NAME, D, NW, BN, QT, SCHED, ST, OCC)                                   \
-  Variant {                                                                            \
-    NAME, D, 32 * QT * NW, BN, NW, Tile<D, NW, BN, QT, ST>::LDS_BYTES,                 \
-        &launch<D, NW, BN, QT, SCHED, ST, OCC>                                         \
+Table table(int i) {
+  Table t;
+  t.v = i == 0 ? attn_fwd_impl::variants_d64(&t.n)
+               : i == 1 ? attn_fwd_impl::variants_d128(&t.n) : attn_fwd_impl::variants_d256(&t.n);
+  return t;
+}
+int num_variants() { return table(0).n + table(1).n + table(2).n; }
+const Variant* variant(int id) {
+  if (id < 0) return nullptr;
+  for (int i = 0; i < 3; ++i) {
+    const Table t = table(i);
+    if (id < t.n) return t.v + id;
+    id -= t.n;
   }
+  return nullptr;
+}
 
-// Name fields: head dim, query rows per workgroup, keys per block, waves,
-// query tiles per wave, LDS ring slots, workgroups per CU (occ), schedule.
-const Variant kVariants[] = {
-    VARIANT("d64_bm256_bn64_w8_q1_st2_occ1_simple", 64, 8, 64, 1, kSimple, 2, 1),         // 0
-    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_simple", 128, 8, 64, 1, kSimple, 2, 1),       // 1
-    VARIANT("d256_bm128_bn64_w4_q1_st2_occ1_simple", 256, 4, 64, 1, kSimple, 2, 1),       // 2
-    VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_simple", 128, 4, 64, 1, kSimple, 2, 2),       // 3
-    VARIANT("d64_bm128_bn64_w4_q1_st2_occ2_simple", 64, 4, 64, 1, kSimple, 2, 2),         // 4
-    VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_simple", 64, 4, 64, 1, kSimple, 2, 3),         // 5
-    VARIANT("d256_bm128_bn32_w4_q1_st2_occ2_simple", 256, 4, 32, 1, kSimple, 2, 2),       // 6
-    VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_simple", 256, 4, 32, 1, kSimple, 2, 1),       // 7
-    VARIANT("d128_bm128_bn64_w4_q1_st3_occ1_simple", 128, 4, 64, 1, kSimple, 3, 1),       // 8
-    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pingpong", 128, 8, 64, 1, kPingPong, 2, 1),   // 9
-    VARIANT("d128_bm256_bn64_w8_q1_st2_occ1_pipe", 128, 8, 64, 1, kPipelined, 2, 1),      // 10
-    VARIANT("d64_bm256_bn64_w8_q1_st2_occ1_pipe", 64, 8, 64, 1, kPipelined, 2, 1),        // 11
-    VARIANT("d128_bm256_bn64_w4_q2_st2_occ1_simple", 128, 4, 64, 2, kSimple, 2, 1),       // 12
-    VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_simple", 128, 8, 32, 1, kSimple, 2, 1),       // 13
-    VARIANT("d128_bm256_bn32_w8_q1_st2_occ1_pipe", 128, 8, 32, 1, kPipelined, 2, 1),      // 14
-    VARIANT("d64_bm128_bn32_w4_q1_st2_occ1_simple", 64, 4, 32, 1, kSimple, 2, 1),         // 15
-    VARIANT("d128_bm256_bn128_w8_q1_st2_occ1_pingpong", 128, 8, 128, 1, kPingPong, 2, 1), // 16
-    VARIANT("d128_bm256_bn128_w8_q1_st2_occ1_simple", 128, 8, 128, 1, kSimple, 2, 1),     // 17
-    VARIANT("d256_bm128_bn64_w4_q1_st2_occ1_pipe", 256, 4, 64, 1, kPipelined, 2, 1),      // 18
-    VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_pipe", 64, 4, 64, 1, kPipelined, 2, 3),        // 19
-    VARIANT("d128_bm128_bn64_w4_q1_st2_occ2_pipe", 128, 4, 64, 1, kPipelined, 2, 2),      // 20
-    VARIANT("d256_bm128_bn32_w4_q1_st2_occ1_pipe", 256, 4, 32, 1, kPipelined, 2, 1),      // 21
-    VARIANT("d64_bm128_bn128_w4_q1_st2_occ2_simple", 64, 4, 128, 1, kSimple, 2, 2),       // 22
-    VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_pipe", 128, 4, 32, 2, kPipelined, 2, 1),      // 23
-    VARIANT("d128_bm256_bn32_w4_q2_st2_occ1_simple", 128, 4, 32, 2, kSimple, 2, 1),       // 24
-    VARIANT("d64_bm256_bn64_w4_q2_st2_occ2_simple", 64, 4, 64, 2, kSimple, 2, 2),         // 25
-    VARIANT("d64_bm256_bn128_w4_q2_st2_occ1_simple", 64, 4, 128, 2, kSimple, 2, 1),       // 26
-    VARIANT("d128_bm256_bn32_w4_q2_st4_occ1_pipe", 128, 4, 32, 2, kPipelined, 4, 1),      // 27
-};
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-// Measured choice per head dimension on MI355X (the same for both masks):
-// the 8-wave ping-pong with 128-key blocks for d = 128; for d = 64, 4-wave
-// workgroups with two query tiles per wave, two workgroups per CU; for
-// d = 256, 4-wave workgroups (O alone takes 128 registers) with the in-wave
-// pipelined schedule and 64-key blocks.
+// The measured default per head dimension (the same for both masks).
 int default_variant(int d, int causal) {
-  switch (d) {
-    case 64: return 25;
-    case 128: return 16;
-    case 256: return 18;
-    default: return -1;
+  (void)causal;
+  for (int id = 0, n = num_variants(); id < n; ++id) {
+    const Variant* v = variant(id);
+    if (v->d == d && v->is_default) return id;
   }
+  return -1;
 }
 
 int validate(const void* q, const void* k, const void* v, const float* out, const float* lse,
@@ -676,7 +90,7 @@ int validate(const void* q, const void* k, const void* v, const float* out, cons
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEAD_DIM;
   uint32_t sbits;
   memcpy(&sbits, &scale, sizeof sbits);  // bit test: immune to fast-math folding
-  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_BAD_SCALE;  // NaN or +-Inf
   long long bh = 0, rows = 0, elems = 0, grid = 0;
   if (__builtin_mul_overflow((long long)B, (long long)H, &bh) ||
       __builtin_mul_overflow(bh, (long long)N, &rows) ||
@@ -694,13 +108,13 @@ int validate(const void* q, const void* k, const void* v, const float* out, cons
 
 int run_variant(int id, const void* q, const void* k, const void* v, float* out, float* lse, int B,
                 int H, int N, int d, int causal, float scale, void* stream) {
-  if (id < 0 || id >= kNumVariants) return ATTN_ERR_BAD_VARIANT;
-  const Variant& var = kVariants[id];
-  int st = validate(q, k, v, out, lse, B, H, N, d, scale, var.bm);
+  const Variant* var = variant(id);
+  if (!var) return ATTN_ERR_BAD_SHAPE;
+  int st = validate(q, k, v, out, lse, B, H, N, d, scale, var->bm);
   if (st != ATTN_OK) return st;
-  if (var.d != d) return ATTN_ERR_BAD_VARIANT;
+  if (var->d != d) return ATTN_ERR_BAD_SHAPE;
   if (B == 0 || H == 0 || N == 0) return ATTN_OK;
-  hipError_t e = var.fn(q, k, v, out, lse, B, H, N, causal, scale, (hipStream_t)stream);
+  hipError_t e = var->fn(q, k, v, out, lse, B, H, N, causal, scale, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -723,32 +137,32 @@ const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL_PTR: return "null pointer argument";
-    case ATTN_ERR_BAD_SHAPE: return "bad shape (negative size or size overflow)";
-    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (need 64, 128 or 256)";
-    case ATTN_ERR_BAD_SCALE: return "scale must be finite and nonzero";
-    case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape (negative size, size overflow, or a variant id that is out of range or serves another head dimension)";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension";
+    case ATTN_ERR_BAD_SCALE: return "scale must be finite";
+    case ATTN_ERR_MISALIGNED: return "pointer misaligned (16 bytes; 4 for lse and the backward's per-row statistics)";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
-    case ATTN_ERR_BAD_VARIANT: return "bad kernel variant id for this head dimension";
-    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_size reports";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than the entry point's workspace-size function reports";
     default: return "unknown status";
   }
 }
 
-int attn_num_variants(void) { return kNumVariants; }
+int attn_num_variants(void) { return num_variants(); }
 
 const char* attn_variant_name(int id) {
-  return (id >= 0 && id < kNumVariants) ? kVariants[id].name : nullptr;
+  const Variant* v = variant(id);
+  return v ? v->name : nullptr;
 }
 
 int attn_variant_info(int id, int* head_dim, int* block_m, int* block_n, int* waves,
                       int* lds_bytes) {
-  if (id < 0 || id >= kNumVariants) return ATTN_ERR_BAD_VARIANT;
-  const Variant& v = kVariants[id];
-  if (head_dim) *head_dim = v.d;
-  if (block_m) *block_m = v.bm;
-  if (block_n) *block_n = v.bn;
-  if (waves) *waves = v.waves;
-  if (lds_bytes) *lds_bytes = v.lds;
+  const Variant* v = variant(id);
+  if (!v) return ATTN_ERR_BAD_SHAPE;
+  if (head_dim) *head_dim = v->d;
+  if (block_m) *block_m = v->bm;
+  if (block_n) *block_n = v->bn;
+  if (waves) *waves = v->waves;
+  if (lds_bytes) *lds_bytes = v->lds;
   return ATTN_OK;
 }
 

@@ -8,8 +8,8 @@ namespace {
 
 // ---------------------------------------------------------------- MLA decoding
 // Multi-head latent attention decoding in the absorbed form (the decoding
-// operator the PipeThreader-and-TileLang page cites as a short TileLang
-// program): all H query heads of a sequence attend to one shared cache of
+// operator the PipeThreader summary page's "Discussion" paragraph cites,
+// written there in about 80 lines against 500-plus by hand): all H query heads of a sequence attend to one shared cache of
 // latent rows of Dk = 576 values (512 latent + 64 rotary); a row's first
 // Dv = 512 values are its value. Split over key chunks like attn_fwd_decode
 // (normalised partials merged by LSE weights), but a workgroup serves 64
@@ -49,7 +49,7 @@ constexpr int kMlaXchg = 4 * 64 * 64;     // partial-S exchange: 64 bytes per la
 __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
                                                             const uint16_t* __restrict__ KV,
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
-                                                            int N, int H, int nc, float c_log2, int negate_q) {
+                                                            int N, int H, int nc, float c_log2, int q_mode) {
   static_assert(kMlaCopies % 4 == 0, "copies split evenly over four waves");
   __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg];
   const int lane = threadIdx.x & 63, hl = lane >> 5, lq = lane & 31, ci = lane & 15;
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
 #pragma unroll
     for (int kk = 0; kk < kMlaHalfK; ++kk) {
       u32x4 raw = *(const u32x4*)(qp + kk * 16);
-      if (negate_q) raw ^= 0x80008000u;
+      raw = apply_q_mode(raw, q_mode);
       qf[0][kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -273,7 +273,7 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   if (st != ATTN_OK) return st;
   uint32_t sbits;
   memcpy(&sbits, &scale, sizeof sbits);
-  if ((sbits & 0x7f800000u) == 0x7f800000u || (sbits & 0x7fffffffu) == 0) return ATTN_ERR_BAD_SCALE;
+  if ((sbits & 0x7f800000u) == 0x7f800000u) return ATTN_ERR_BAD_SCALE;  // NaN or +-Inf
   if (p.rows == 0) return ATTN_OK;
   if (!q || !kv || !out || !lse || !workspace) return ATTN_ERR_NULL_PTR;
   const uintptr_t m = (uintptr_t)q | (uintptr_t)kv | (uintptr_t)out | (uintptr_t)workspace;
@@ -282,8 +282,8 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   float* ws_o = (float*)workspace;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * kMlaDv;
   hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)p.groups, (unsigned)p.nc), dim3(256), 0, (hipStream_t)stream,
-                     (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, fabsf(scale) * kLog2e,
-                     (int)(scale < 0.f));
+                     (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
+                     scale_args(scale).q_mode);
   hipLaunchKernelGGL(mla_combine, dim3((unsigned)p.rows), dim3(256), 0, (hipStream_t)stream, (const float*)ws_o,
                      (const float*)ws_lse, out, lse, (int)p.rows, p.nc);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

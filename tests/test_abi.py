@@ -52,8 +52,13 @@ def test_validation_happens_before_any_hip_call(attn):
     assert attn.attn_fwd(*good, 1, 1, -16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
     for d in (0, 32, 96, 192, 512):
         assert attn.attn_fwd(*good, 1, 1, 16, d, 0, 0.1, None) == attn.ATTN_ERR_HEAD_DIM
-    for s in (float("nan"), float("inf"), float("-inf"), 0.0):
+    for s in (float("nan"), float("inf"), float("-inf")):
         assert attn.attn_fwd(*good, 1, 1, 16, 128, 0, s, None) == attn.ATTN_ERR_BAD_SCALE
+    # zero and negative scales pass validation (the next check, alignment, fires)
+    for s in (0.0, -0.0, -0.5):
+        assert attn.attn_fwd(P + 2, P, P, P, P, 1, 1, 16, 128, 0, s, None) == attn.ATTN_ERR_MISALIGNED
+    # lse needs only 4-byte alignment, every other buffer 16
+    assert attn.attn_fwd(P, P, P, P, P + 2, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_MISALIGNED
     assert attn.attn_fwd(P + 2, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_MISALIGNED
     assert attn.attn_fwd(P, P, P, P + 8, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_MISALIGNED
     # empty problems are a no-op success, even with null pointers
@@ -87,6 +92,7 @@ def test_decode_validation_happens_before_any_hip_call(attn):
     assert call(d=192) == attn.ATTN_ERR_HEAD_DIM
     assert call(Nkv=0) == attn.ATTN_ERR_BAD_SHAPE
     assert call(s=float("nan")) == attn.ATTN_ERR_BAD_SCALE
+    assert call(s=0.0, k=P + 4) == attn.ATTN_ERR_MISALIGNED  # a zero scale is valid
     assert call(k=P + 4) == attn.ATTN_ERR_MISALIGNED
     assert call(ws=P + 8) == attn.ATTN_ERR_MISALIGNED
     assert call(wsb=need - 1) == attn.ATTN_ERR_WORKSPACE
@@ -115,8 +121,9 @@ def test_bwd_validation_happens_before_any_hip_call(attn):
     assert call(ws=0) == attn.ATTN_ERR_NULL_PTR
     assert call(d=256) == attn.ATTN_ERR_HEAD_DIM
     assert call(N=-1) == attn.ATTN_ERR_BAD_SHAPE
-    for sc in (float("nan"), float("inf"), 0.0):
+    for sc in (float("nan"), float("inf")):
         assert call(s=sc) == attn.ATTN_ERR_BAD_SCALE
+    assert call(s=0.0, do=P + 2) == attn.ATTN_ERR_MISALIGNED  # a zero scale is valid
     assert call(do=P + 2) == attn.ATTN_ERR_MISALIGNED
     assert call(dk=P + 8) == attn.ATTN_ERR_MISALIGNED
     assert call(l=P + 2) == attn.ATTN_ERR_MISALIGNED
@@ -160,6 +167,7 @@ def test_mla_validation_happens_before_any_hip_call(attn):
         assert call(**{kw: 0}) == attn.ATTN_ERR_NULL_PTR, kw
     assert call(H=64 + 32) == attn.ATTN_ERR_BAD_SHAPE
     assert call(s=float("nan")) == attn.ATTN_ERR_BAD_SCALE
+    assert call(s=0.0, kv=P + 8) == attn.ATTN_ERR_MISALIGNED  # a zero scale is valid
     assert call(kv=P + 8) == attn.ATTN_ERR_MISALIGNED
     assert call(l=P + 2) == attn.ATTN_ERR_MISALIGNED
     assert call(wsb=need - 1) == attn.ATTN_ERR_WORKSPACE
@@ -187,15 +195,37 @@ def test_variant_table(attn):
             assert 0 <= vid < n and attn.attn_variant_info(vid)["head_dim"] == d
     assert attn.attn_default_variant(96, 0) == -1
     P = 1 << 20
-    assert attn.attn_fwd_variant(n, P, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_VARIANT
+    assert attn.attn_fwd_variant(n, P, P, P, P, P, 1, 1, 16, 128, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
     d128 = attn.attn_default_variant(128, 0)
-    assert attn.attn_fwd_variant(d128, P, P, P, P, P, 1, 1, 16, 64, 0, 0.1, None) == attn.ATTN_ERR_BAD_VARIANT
+    assert attn.attn_fwd_variant(d128, P, P, P, P, P, 1, 1, 16, 64, 0, 0.1, None) == attn.ATTN_ERR_BAD_SHAPE
+
+
+def header_status_codes():
+    text = open(HEADER).read()
+    enum = text[text.index("enum attn_status"):]
+    enum = re.sub(r"/\*.*?\*/", "", enum[:enum.index("};")], flags=re.S)
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_\w+)\s*=\s*(\d+)", enum)}
+
+
+def test_status_codes_match_the_header(attn):
+    codes = header_status_codes()
+    # the codes of the boundary contract, plus the workspace code of the
+    # entries that take one
+    assert codes == {"ATTN_OK": 0, "ATTN_ERR_NULL_PTR": 1, "ATTN_ERR_BAD_SHAPE": 2, "ATTN_ERR_HEAD_DIM": 3,
+                     "ATTN_ERR_BAD_SCALE": 4, "ATTN_ERR_MISALIGNED": 5, "ATTN_ERR_HIP": 6,
+                     "ATTN_ERR_WORKSPACE": 8}
+    for name, value in codes.items():
+        assert getattr(attn, name) == value, name
+    assert not hasattr(attn, "ATTN_ERR_BAD_VARIANT")
 
 
 def test_strerror_covers_every_status(attn):
-    for st in range(9):
+    for st in header_status_codes().values():
         assert attn.attn_strerror(st) and attn.attn_strerror(st) != "unknown status"
+    assert attn.attn_strerror(7) == "unknown status"
     assert attn.attn_strerror(99) == "unknown status"
+    # the workspace message names no single entry point
+    assert "decode" not in attn.attn_strerror(attn.ATTN_ERR_WORKSPACE)
 
 
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):

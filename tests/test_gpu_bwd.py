@@ -7,14 +7,17 @@ forward itself in fp64.
 
 Acceptance bar, per gradient X in (dq, dk, dv), relative to the reference's
 own scale (the gradients' magnitudes vary with N and d):
-    max |X - X_ref|  <= 2e-2 * max |X_ref|  + 1e-5
+    max |X - X_ref|  <= 1e-2 * max |X_ref|  + 1e-5
     mean |X - X_ref| <= 5e-3 * mean |X_ref| + 1e-5
 The products run on bf16 operands with fp32 accumulation; P and dS are
-rounded to bf16 (relative error up to 2^-9 per term) before the dV, dK and
-dQ contractions, which sets the scale of the relative terms. The absolute
-floor covers gradients that vanish in exact arithmetic (one visible key:
-dP - D = 0), where the fp32 difference of two O(10) dot products leaves
-O(1e-6) residue.
+rounded to bf16 (relative error up to 2^-9 = 1.95e-3 per term, rms
+2^-9/sqrt(3) = 1.1e-3) before the dV, dK and dQ contractions. A gradient
+element is a sum of many such terms of mixed sign, so its relative error has
+about the per-term rms, 1-2e-3 (the mean bar, 5e-3, leaves 2.5x over that);
+the worst element over a few million is a few rms, 3-4e-3 measured, under
+the max bar with 2.5x to spare. The absolute floor covers gradients that
+vanish in exact arithmetic (one visible key: dP - D = 0), where the fp32
+difference of two O(10) dot products leaves O(1e-6) residue.
 """
 
 import sys
@@ -28,7 +31,7 @@ from gpu_helpers import ensure_built, to_device
 
 pytestmark = pytest.mark.gpu
 
-GRAD_MAX_REL = 2e-2
+GRAD_MAX_REL = 1e-2
 GRAD_MEAN_REL = 5e-3
 GRAD_ABS_FLOOR = 1e-5
 
@@ -108,7 +111,7 @@ def test_bwd_negative_scale_and_stress_keys(oracle_mod):
     q, k, v = I.gen_qkv(B, H, N, d, seed=71, key_stress=True)
     do = I.gen_dout(B, H, N, d, seed=71)
     for causal in (False, True):
-        for scale in (np.float32(-0.125), np.float32(0.125)):
+        for scale in (np.float32(-0.125), np.float32(0.125), np.float32(0.0)):
             got = run_bwd(q, k, v, do, causal, scale)
             ref = oracle_mod.attn_bwd(q, k, v, do, causal, scale)
             compare_grads(got, ref, f"bwd scale {scale} causal {causal}")
@@ -149,25 +152,26 @@ def test_bwd_many_heads_wide_dkdv_workgroups(oracle_mod, causal):
 
 def test_bwd_workload_16k_sampled(oracle_mod):
     """The N=16384 d=128 workload at full size, as the benchmark times it:
-    dQ on sampled rows of every head, dK and dV on sampled key rows of the
-    last head."""
+    dQ on sampled rows of every head, dK and dV on sampled key rows of every
+    head."""
     cfg = I.HEADLINE
     _say(f"case bwd workload {cfg.name}")
-    _sampled_parity(oracle_mod, cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, cfg.seed, (cfg.B * cfg.H - 1,), cfg.name)
+    _sampled_parity(oracle_mod, cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, cfg.seed, tuple(range(cfg.B * cfg.H)),
+                    cfg.name)
 
 
 def test_bwd_workload_d64_causal_8k_sampled(oracle_mod):
     """The causal N=8192 d=64 workload with every 7th key scaled by 8, at full
-    size as the benchmark times it: dQ on sampled rows of every head, dK and
-    dV on sampled key rows of the first and last heads."""
+    size as the benchmark times it: dQ and dK/dV on sampled rows of every
+    head."""
     cfg = I.CAUSAL_8K_STRESS
     _say(f"case bwd workload {cfg.name}")
     q, k, v = I.gen_config(cfg)
     do = I.gen_dout(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed)
     got = [x.reshape(-1, cfg.d) for x in run_bwd(q, k, v, do, cfg.causal, cfg.scale)]
     qrows = I.sample_rows(cfg.B, cfg.H, cfg.N, per_head=3, seed=51)
-    heads = (0, cfg.B * cfg.H - 1)
-    krows = np.concatenate([h * cfg.N + I.sample_rows(1, 1, cfg.N, per_head=16, seed=52 + h) for h in heads])
+    heads = range(cfg.B * cfg.H)
+    krows = np.concatenate([h * cfg.N + I.sample_rows(1, 1, cfg.N, per_head=6, seed=52 + h) for h in heads])
     dq, dk, dv = oracle_mod.attn_bwd_rows(q, k, v, do, cfg.causal, cfg.scale, qrows, krows)
     compare_grads((got[0][qrows], got[1][krows], got[2][krows]), (dq, dk, dv), cfg.name)
 

@@ -4,12 +4,13 @@ Every call goes through the C ABI; inputs come from the seeded generator and
 expected values only from the oracle.
 
 Acceptance bar, relative to the reference's own scale:
-    max |out - ref|  <= 2e-2 * max |ref|  + 1e-5
+    max |out - ref|  <= 1e-2 * max |ref|  + 1e-5
     mean |out - ref| <= 5e-3 * mean |ref| + 1e-5
 x and cb are exact bf16 and the products accumulate in fp32; the scaled
 matrix A = cb * exp(decay) * dt is rounded to bf16 (relative error up to
-2^-9 per term) before the contraction with x, which sets the relative terms;
-exp2 on v_exp_f32 adds about 1e-7.
+2^-9 per term, rms 1.1e-3) before the contraction with x, so an output
+element's relative error is about that rms and the worst of millions a few
+times it (2.8e-3 measured); exp2 on v_exp_f32 adds about 1e-7.
 """
 
 import sys
@@ -23,7 +24,7 @@ from gpu_helpers import ensure_built
 
 pytestmark = pytest.mark.gpu
 
-CS_MAX_REL = 2e-2
+CS_MAX_REL = 1e-2
 CS_MEAN_REL = 5e-3
 CS_ABS_FLOOR = 1e-5
 

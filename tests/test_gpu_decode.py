@@ -92,7 +92,7 @@ def test_decode_negative_scale_and_stress_keys(oracle_mod):
     kf = I.bf16_bits_to_f32(k)
     kf[:, :, ::7, :] *= np.float32(8.0)
     k = I.f32_to_bf16_bits(kf)
-    for scale in (np.float32(-0.125), np.float32(0.125)):
+    for scale in (np.float32(-0.125), np.float32(0.125), np.float32(0.0)):
         out, lse = run_decode(q, k, v, scale)
         ro, rl = oracle_mod.attn_decode(q, k, v, scale)
         _say(str(compare(out, lse, ro, rl, f"decode scale {scale}")))

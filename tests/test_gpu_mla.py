@@ -72,7 +72,8 @@ def test_mla_negative_scale_and_reuse(oracle_mod):
     from software_pipelined_amd import attn
     st, need = attn.mla_decode_workspace_size(2, 128, 3000)
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
-    for shape, scale in (((2, 128, 3000), np.float32(-0.09)), ((1, 64, 77), np.float32(0.2))):
+    for shape, scale in (((2, 128, 3000), np.float32(-0.09)), ((1, 64, 77), np.float32(0.2)),
+                         ((1, 64, 300), np.float32(0.0))):
         B, H, N = shape
         _say(f"case mla reuse {shape} scale {scale}")
         q, kv = I.gen_mla(B, H, N, 576, seed=17 + N)
