@@ -50,6 +50,11 @@ def load_library():
     if not os.path.exists(LIB_PATH):
         raise FileNotFoundError(
             f"{LIB_PATH} is missing: build it first (python -m software_pipelined_amd.build)")
+    # torch first: its bundled HIP runtime has the same soname as the one the
+    # library links, so loaded first it serves both. Loaded the other way
+    # round, the process holds two HIP runtimes, and torch's device pointers
+    # and streams are foreign to the library's (every launch then fails).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = _FWD_ARGS

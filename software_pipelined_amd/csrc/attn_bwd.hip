@@ -23,15 +23,15 @@ namespace {
 // deterministic).
 //
 // Layout tricks shared by both main kernels: a [rows][d] block image in LDS
-// (K-style XOR swizzle) serves both as row-fragment A operand
-// (ds_read_b128) and, through ds_read_b64_tr_b16, as the transposed A
+// (swz_dual, conflict-free for both reads) serves both as row-fragment A
+// operand (ds_read_b128) and, through ds_read_b64_tr_b16, as the transposed A
 // operand; an MFMA accumulator tile converted to bf16 is the B operand of the
 // next product without an LDS round trip.
 
 constexpr int kBwdRows = 32;               // query rows per statistics block
 constexpr int kBwdStatBytes = 2 * kBwdRows * 4;  // log2e*LSE then D, fp32
 
-// Compact fragment offsets into a K-swizzled [rows][D] image, one or two
+// Compact fragment offsets into a swz_dual [rows][D] image, one or two
 // registers per lane instead of one per fragment: the swizzle only permutes
 // 16-byte chunks within a row, so every fragment's offset is one lane base
 // XOR a compile-time constant (the row part and the chunk part occupy
@@ -39,45 +39,80 @@ constexpr int kBwdStatBytes = 2 * kBwdRows * 4;  // log2e*LSE then D, fp32
 //   row fragment kk (A operand, ds_read_b128): row lq, chunk 2kk + h
 //       = kbase ^ (32 kk);
 //   transposed read (t, r) (ds_read_b64_tr_b16, as LdsOffsets::v): rows
-//       r0 + 8r carry different swizzles, so two bases; dims tile t
-//       = tbase[r] ^ (64 t); adding 16p rows leaves the swizzle unchanged.
+//       r0 + 8r, r0 < 8; swz_dual(r0 + 8) = swz_dual(r0) ^ 2, so the second
+//       base is tbase ^ 32; dims tile t = base ^ (64 t); adding 16p rows
+//       leaves the swizzle unchanged.
 template <int D>
 struct BwdOffsets {
-  int kbase, tbase0, tbase1;
+  int kbase, tbase;
   __device__ __forceinline__ explicit BwdOffsets(int lane) {
     const int h = lane >> 5, lq = lane & 31, ci = lane & 15, g2 = (lane >> 4) & 1;
-    kbase = lq * (D * 2) + ((h ^ swz_k<D>(lq)) << 4);
+    kbase = lq * (D * 2) + ((h ^ swz_dual<D>(lq)) << 4);
     const int r0 = 4 * h + (ci >> 2), c1 = 2 * g2 + ((ci & 3) >> 1);
-    tbase0 = r0 * (D * 2) + ((c1 ^ swz_k<D>(r0)) << 4) + 8 * (ci & 1);
-    tbase1 = r0 * (D * 2) + ((c1 ^ swz_k<D>(r0 + 8)) << 4) + 8 * (ci & 1);
+    tbase = r0 * (D * 2) + ((c1 ^ swz_dual<D>(r0)) << 4) + 8 * (ci & 1);
   }
   __device__ __forceinline__ int k(int kk) const { return kbase ^ (32 * kk); }
+  __device__ __forceinline__ int t(int r, int tt) const { return tbase ^ (32 * r) ^ (64 * tt); }
 };
 
-// A operand of X^T[dim tile t][rows 16p .. 16p+15] from a K-swizzled image.
+// mma_qk from a swz_dual image (as qk_block): S^T[key][query] for BN rows of
+// the image against Q^T fragments held in registers.
+template <int D, int BN>
+__device__ __forceinline__ void qk_block_dual(const char* img, const BwdOffsets<D>& bo, const bf16x8 (&qf)[1][D / 16],
+                                              f32x16 (&s)[1][BN / 32]) {
+  constexpr int NKB = BN / 32;
+  bf16x8 kf[D / 16][NKB];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[kk][kb] = *(LDS_AS const bf16x8*)(img + bo.k(kk) + kb * 32 * (D * 2));
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) s[0][kb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[0][kk], s[0][kb], 0, 0, 0);
+}
+
+// A operand of X^T[dim tile t][rows 16p .. 16p+15] from a swz_dual image.
 template <int D>
 __device__ __forceinline__ bf16x8 read_tr_k(const char* img, const BwdOffsets<D>& bo, int t, int p) {
-  const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + (bo.tbase0 ^ (64 * t)) + (p * 16) * (D * 2)));
-  const i16x4 a1 =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + (bo.tbase1 ^ (64 * t)) + (p * 16 + 8) * (D * 2)));
+  const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + bo.t(0, t) + (p * 16) * (D * 2)));
+  const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(img + bo.t(1, t) + (p * 16 + 8) * (D * 2)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Workgroup-shared HBM -> LDS copy t of a BN-row block (same placement as
-// issue_copy, K swizzle), in inline assembly so that the compiler's
+// Workgroup-shared HBM -> LDS copy t of a BN-row block (placement as
+// issue_copy, swz_dual), in inline assembly so that the compiler's
 // conservative wait before transposed LDS reads does not drain the copies of
 // the next block; callers wait with wait_vmcnt.
 template <int D, int NW, int BN>
 __device__ __forceinline__ void issue_copy_asm(const uint16_t* __restrict__ src, int row0, int N, char* dst,
                                                int wave, int lane, int t) {
-  cs_dma(block_rsrc<D, BN>(src, row0, N), (int)block_lane_offset<D, NW, BN, false>(t, wave, lane),
+  cs_dma(block_rsrc<D, BN>(src, row0, N), (int)block_lane_offset_sw<D, NW, BN, 2>(t, wave, lane),
          dst + (t * NW + wave) * 64 * 16);
+}
+
+// The lane index from mbcnt, in a volatile asm block the compiler can neither
+// hoist nor merge: values derived from it inside the block loop are
+// recomputed there each block rather than kept live across the loop. When
+// such a value is spilled instead, its scratch reload at the top of a block
+// comes with a vmcnt wait that also drains the next block's copies.
+__device__ __forceinline__ int opaque_lane() {
+  int v;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 %0, -1, %0"
+      : "=v"(v));
+  return v;
 }
 
 // One 256-byte statistics block into a wave's own 1 KiB LDS slot (lanes past
 // the block read zeros).
-__device__ __forceinline__ void issue_stat_copy(const float* src, char* dst, int lane) {
-  cs_dma(__builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBwdStatBytes, kRsrcWord3), lane * 16, dst);
+__device__ __forceinline__ void issue_stat_copy(const float* src, char* dst) {
+  cs_dma(__builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, kBwdStatBytes, kRsrcWord3), opaque_lane() * 16,
+         dst);
 }
 
 // stats[bh][blk] = { log2e * LSE of the block's 32 rows, D of those rows };
@@ -144,7 +179,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
   bf16x8 kf[1][D / 16], vf[1][D / 16];
   load_q<D, 1>(K + head, k0w, N, q_mode, kf, lane);  // K as scale_args takes it
   load_q<D, 1>(V + head, k0w, N, 0, vf, lane);
-  const BwdOffsets<D> bo(lane);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) dk[t] = dv[t] = f32x16{};
@@ -156,12 +190,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
       issue_copy_asm<D, NW, BQ>(Q + head, jb * BQ, N, base, wave, lane, t);
       issue_copy_asm<D, NW, BQ>(dO + head, jb * BQ, N, base + MAT, wave, lane, t);
     }
-    issue_stat_copy(st_head + (size_t)jb * (2 * BQ), base + 2 * MAT + wave * STAT, lane);
+    issue_stat_copy(st_head + (size_t)jb * (2 * BQ), base + 2 * MAT + wave * STAT);
   };
 
   const int jb0 = CAUSAL ? min(k0 / BQ, nqb) : 0;  // earlier query blocks see none of these keys
   if (jb0 < nqb) copy_stage(jb0, 0);
-  const int key = k0w + (lane & 31);
   for (int jb = jb0; jb < nqb; ++jb) {
     const int slot = (jb - jb0) & 1;
     wait_vmcnt<0>();
@@ -169,9 +202,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
     if (jb + 1 < nqb) copy_stage(jb + 1, slot ^ 1);
     const char* Qs = smem + slot * STAGE;
     const char* dOs = Qs + MAT;
-    const char* Ss = Qs + 2 * MAT + wave * STAT;
     const int q0 = jb * BQ;
     if (CAUSAL && q0 + BQ - 1 < k0w) continue;  // wave-uniform: every query precedes every key of this wave
+    // d = 128: per-lane offsets rebuilt each block (opaque_lane), so nothing
+    // lane-derived stays live across the loop next to the K/V operands and
+    // the accumulators (256 registers with two waves per SIMD). d = 64 has
+    // room and keeps them loop-invariant.
+    const int ln = D >= 128 ? opaque_lane() : lane, hl = ln >> 5, key = k0w + (ln & 31);
+    const BwdOffsets<D> bo(ln);
+    const char* Ss = Qs + 2 * MAT + wave * STAT;
     // fragments are read right before the MFMA that consumes them: with two
     // waves per SIMD the K/V operands and dK/dV accumulators leave little room
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -184,14 +223,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
     const bool diag = CAUSAL && q0 < k0w + 31;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l2 = *(LDS_AS const f32x4*)(Ss + (8 * g + 4 * h) * 4);
-      const f32x4 dd = *(LDS_AS const f32x4*)(Ss + BQ * 4 + (8 * g + 4 * h) * 4);
+      const f32x4 l2 = *(LDS_AS const f32x4*)(Ss + (8 * g + 4 * hl) * 4);
+      const f32x4 dd = *(LDS_AS const f32x4*)(Ss + BQ * 4 + (8 * g + 4 * hl) * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2[i]));
         if (diag) {
-          const int qi = q0 + 8 * g + 4 * h + i;
+          const int qi = q0 + 8 * g + 4 * hl + i;
           p = key > qi ? 0.f : p;
         }
         s[r] = p;
@@ -212,6 +251,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
       }
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+  const int key = k0w + (lane & 31);
   if (key < N) {
     float* krow = dK + head + (size_t)key * D;
     float* vrow = dV + head + (size_t)key * D;
@@ -258,7 +298,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
   const int qs = min(qi, nqb * kBwdRows - 1);  // rows past N: padded statistics (+inf, 0)
   const float* st = stats + ((size_t)bh * nqb + qs / kBwdRows) * (2 * kBwdRows);
   const float l2 = st[qs % kBwdRows], dd = st[kBwdRows + qs % kBwdRows];
-  const LdsOffsets<D> off(lane);
   const BwdOffsets<D> bo(lane);
   f32x16 dq[D / 32];
 #pragma unroll
@@ -286,8 +325,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
     const char* Ks = smem + slot * STAGE;
     const char* Vs = Ks + MAT;
     f32x16 s[1][BN / 32], dp[1][BN / 32];
-    qk_block<D, BN, 1>(Ks, off, qf, s);
-    qk_block<D, BN, 1>(Vs, off, gf, dp);
+    qk_block_dual<D, BN>(Ks, bo, qf, s);
+    qk_block_dual<D, BN>(Vs, bo, gf, dp);
     if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > q0w)) mask_block<BN, 1, CAUSAL>(s, kv0, qi, N, lane);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -364,6 +403,7 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   const int neg = sa.q_mode;
   const unsigned gp = (unsigned)(p.bh * p.nqb);
   const unsigned gk = (unsigned)(p.bh * p.n_ktiles), gq = (unsigned)(p.bh * p.n_qtiles);
+  clear_last_hip_error();
   hipLaunchKernelGGL((attn_bwd_prep<D>), dim3(gp), dim3(256), 0, stream, o, (const uint16_t*)dout, lse, stats, N,
                      p.nqb);
   if (D == 128 && p.kw == 8)

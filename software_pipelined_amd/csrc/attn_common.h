@@ -77,6 +77,16 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) {
   return D == 64 ? (((row >> 1) & 1) << 2) : ((row & 3) << 2);
 }
+// For an image read both ways (row fragments and transposed reads, as the
+// backward's Q, dO and K images are): a permutation of the 16 chunk columns
+// over 16 consecutive rows (row fragments conflict-free, as swz_k) whose bits
+// 2-3 differ between the 4 rows of every aligned group (transposed reads
+// conflict-free, as swz_v). At d = 64 a 256-byte bank line holds two rows,
+// so the same holds per row pair.
+template <int D>
+__device__ __forceinline__ int swz_dual(int row) {
+  return D == 64 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
 
 // HBM -> LDS copies of BN-row blocks of one [N][D] matrix. Every wave moves
 // LOADS x 1 KiB per block; lane l's 16 bytes land at dst + 16*l, so the
@@ -87,14 +97,24 @@ __device__ __forceinline__ int swz_v(int row) {
 // beyond its fixed lane offset.
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-template <int D, int NW, int BN, bool IS_V>
-__device__ __forceinline__ uint32_t block_lane_offset(int t, int wave, int lane) {
+// Swizzle kinds: 0 = swz_k, 1 = swz_v, 2 = swz_dual.
+template <int D, int SW>
+__device__ __forceinline__ int swz(int row) {
+  return SW == 0 ? swz_k<D>(row) : SW == 1 ? swz_v<D>(row) : swz_dual<D>(row);
+}
+
+template <int D, int NW, int BN, int SW>
+__device__ __forceinline__ uint32_t block_lane_offset_sw(int t, int wave, int lane) {
   using T = Tile<D, NW, BN>;
   const int p = (t * NW + wave) * 64 + lane;
   const int row = p / T::RC;
   const int pc = p % T::RC;
-  const int c = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+  const int c = pc ^ swz<D, SW>(row);
   return (uint32_t)(row * (D * 2) + c * 16);
+}
+template <int D, int NW, int BN, bool IS_V>
+__device__ __forceinline__ uint32_t block_lane_offset(int t, int wave, int lane) {
+  return block_lane_offset_sw<D, NW, BN, IS_V ? 1 : 0>(t, wave, lane);
 }
 
 // row0 < N always (callers clamp block indices to the last block). The byte
@@ -475,6 +495,11 @@ __host__ __device__ inline ScaleArgs scale_args(float scale) {
   return ScaleArgs{fabsf(scale) * kLog2e, scale < 0.f ? 1 : 0};
 }
 
+// HIP keeps one "last error" per host thread, set by any failing runtime call
+// (the caller's included). Entry points clear it right before their launches,
+// so that the hipGetLastError after them reports those launches only.
+inline void clear_last_hip_error() { (void)hipGetLastError(); }
+
 // 8 bf16 values as q_mode asks (see scale_args).
 __device__ __forceinline__ u32x4 apply_q_mode(u32x4 raw, int q_mode) {
   if (q_mode == 1) raw ^= 0x80008000u;  // exact sign flip of 8 bf16 values
@@ -559,33 +584,33 @@ struct Ctx {
   float c_log2;
 };
 
-// Workgroup -> (batch*head, query tile) and the per-wave key range.
+// Workgroup -> (batch*head, query tile) and the per-wave key range, for pass
+// `pass` of the workgroup. Without a mask every query tile costs the same and
+// a workgroup takes one. With the causal mask tile t costs t+1 units, so a
+// workgroup takes two: tile n-1-p, then tile p (one when they coincide), and
+// every workgroup gets the same n+1 units: the grid is one balanced round
+// instead of long tiles finishing late. The ids of one head are contiguous in
+// the XCD-remapped order, so its K/V stays in one XCD's L2. Returns false
+// when the workgroup has no tile for this pass (wave-uniform).
 template <int D, int BM, int BN, int WROWS, bool CAUSAL>
-__device__ __forceinline__ Ctx make_ctx(const uint16_t* K, const uint16_t* V, int N, int n_qtiles,
-                                        float c_log2) {
-  Ctx c;
+__device__ __forceinline__ bool make_ctx(const uint16_t* K, const uint16_t* V, int N, int n_qtiles,
+                                         float c_log2, int pass, Ctx& c) {
   c.lane = threadIdx.x & 63;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tile;
   if (CAUSAL) {
-    // Causal tiles differ in length. Heads are taken in groups, each inside
-    // one XCD's contiguous range. Within a group the longest tiles of all its
-    // heads come first (longest processing time first), so no long tile
-    // starts at the end. A group's K/V stays within about twice an XCD's
-    // 4 MB L2: 8 MiB / (K+V bytes per head) heads, at most BH/8. Measured
-    // best on the causal N=2048 d=128, N=8192 d=64 and N=4096 d=256 shapes;
-    // one head per group loses up to 18%, unbounded groups lose L2 reuse
-    // (-24% at N=8192). The last group takes the remaining heads.
-    const int BH = gridDim.x / n_qtiles;
-    const int fit = (int)((8ll << 20) / (4ll * N * D));
-    const int hpg = max(1, min(BH / 8, fit)), span = hpg * n_qtiles, ng = BH / hpg;
-    const int g = L / span;
-    const int h0 = min(g, ng) * hpg, hn = g < ng ? hpg : BH - ng * hpg;
-    const int r = L - min(g, ng) * span;
-    c.bh = h0 + r % hn;
-    tile = n_qtiles - 1 - r / hn;
+    const int np = (n_qtiles + 1) / 2;  // workgroups per head
+    c.bh = L / np;
+    const int p = L % np, heavy = n_qtiles - 1 - p;
+    if (pass == 0) {
+      tile = heavy;
+    } else {
+      if (p == heavy) return false;
+      tile = p;
+    }
   } else {
+    if (pass > 0) return false;
     c.bh = L / n_qtiles;
     tile = L % n_qtiles;
   }
@@ -601,7 +626,12 @@ __device__ __forceinline__ Ctx make_ctx(const uint16_t* K, const uint16_t* V, in
   c.kv_end_w = CAUSAL ? min(N, c.q0w + WROWS) : N;
   c.nblk = (kv_end_wg + BN - 1) / BN;
   c.c_log2 = c_log2;
-  return c;
+  return true;
+}
+
+// Workgroups in the grid of a forward launch (see make_ctx).
+__host__ __device__ inline long long fwd_grid(long long BH, int n_qtiles, int causal) {
+  return BH * (causal ? (n_qtiles + 1) / 2 : n_qtiles);
 }
 
 // Does block j straddle the diagonal (first query of the wave) or the end of K?

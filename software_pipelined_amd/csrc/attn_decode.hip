@@ -243,6 +243,7 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
   const ScaleArgs sa = scale_args(scale);
   const float c = sa.c_log2;
   const int neg = sa.q_mode;
+  clear_last_hip_error();
   float* ws_o = (float*)ws;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * D;
   const dim3 grid((unsigned)(BH * p.n_qt), (unsigned)(p.nc / NW)), block(NW * 64);

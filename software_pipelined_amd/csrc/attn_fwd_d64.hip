@@ -14,6 +14,7 @@ const Variant kTable[] = {
     VARIANT("d64_bm128_bn64_w4_q1_st2_occ3_pipe", 64, 4, 64, 1, kPipelined, 2, 3, false),
     VARIANT("d64_bm128_bn128_w4_q1_st2_occ2_simple", 64, 4, 128, 1, kSimple, 2, 2, false),
     VARIANT("d64_bm256_bn128_w4_q2_st2_occ1_simple", 64, 4, 128, 2, kSimple, 2, 1, false),
+    VARIANT("d64_bm256_bn128_w8_q1_st2_occ1_pingpong1", 64, 8, 128, 1, kPingPong1, 2, 1, false),
 };
 }  // namespace
 

@@ -62,13 +62,11 @@ __device__ __forceinline__ void simple_block(const Ctx& c, char* smem, int j,
 // NW * OCC / 4): with NW = 4 and OCC = 2 two independent workgroups share a
 // CU, so the two waves on each SIMD are never held in step by one barrier.
 template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int OCC>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
+__device__ __forceinline__ void attn_fwd_simple_tile(const Ctx& c, char* smem,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int q_mode) {
   using T = Tile<D, NW, BN, QT, ST>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
 
   // Q first, then blocks 0 .. ST-2 (so the in-loop waits count block copies
   // only); past the last block a clamped duplicate lands in a slot nobody
@@ -101,6 +99,27 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, ms_run, l_run, c.c_log2, c.lane);
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int ST, int OCC>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_simple(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int q_mode) {
+  using T = Tile<D, NW, BN, QT, ST>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  if constexpr (!CAUSAL) {
+    Ctx c;
+    make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, 0, c);
+    attn_fwd_simple_tile<D, NW, BN, QT, CAUSAL, ST, OCC>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+      Ctx c;
+      if (!make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, pass, c)) break;
+      if (pass > 0) block_barrier();  // every wave is done with the ring of the previous tile
+      attn_fwd_simple_tile<D, NW, BN, QT, CAUSAL, ST, OCC>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- pipelined kernel
@@ -288,14 +307,12 @@ __device__ __forceinline__ void pipe_block_generic(const Ctx& c, char* smem, int
 // NW waves, QT query tiles of 32 per wave, BN keys per block, ST ring slots
 // (even: the S buffers swap roles every block).
 template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int ST>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipelined(
+__device__ __forceinline__ void attn_fwd_pipelined_tile(const Ctx& c, char* smem,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int q_mode) {
   static_assert(ST % 2 == 0, "the block loop is unrolled by ST and S alternates by parity");
   using T = Tile<D, NW, BN, QT, ST>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
 
   // prologue: Q; K_0 .. K_{ST-1} and V_0 .. V_{ST-3} in flight; S_0 = Q K_0^T
   bf16x8 qf[QT][D / 16];
@@ -365,6 +382,27 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipeline
     });
   }
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, ms_run, l_run, c.c_log2, c.lane);
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int ST>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pipelined(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int q_mode) {
+  using T = Tile<D, NW, BN, QT, ST>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  if constexpr (!CAUSAL) {
+    Ctx c;
+    make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, 0, c);
+    attn_fwd_pipelined_tile<D, NW, BN, QT, CAUSAL, OCC, ST>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+      Ctx c;
+      if (!make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, pass, c)) break;
+      if (pass > 0) block_barrier();  // every wave is done with the ring of the previous tile
+      attn_fwd_pipelined_tile<D, NW, BN, QT, CAUSAL, OCC, ST>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+    }
+  }
 }
 
 // issue_copy through inline assembly (cs_dma): the compiler does not see the
@@ -502,6 +540,11 @@ __device__ __forceinline__ void fused_pv_qk(const char* Vs, const char* Ks, cons
 // (B); at barrier 2m+1 the copies of K_{m+2} (over K_m) and V_{m+1} (over
 // V_{m-1}) start, and each wave waits for them before barrier 2m+3. Each
 // group runs its own loop; both pass the same number of barriers.
+// SYNC = 2 keeps a barrier between every two intervals. SYNC = 1 keeps only
+// the odd ones: every LDS read of a block falls between the odd barriers
+// around it (K_j in (2j-1, 2j+1), V_j in (2j+1, 2j+3)), so the ring stays
+// safe, and the even barrier only enforced the turn change; without it a
+// wave that ends its turn early starts the next one instead of waiting.
 template <int D, int NW, int BN, int QT, bool CAUSAL, int VS, int KS, typename CopyFn>
 __device__ __forceinline__ void pingpong_mfma_turn(const Ctx& c, char* smem, int jp,
                                                    const LdsOffsets<D>& off,
@@ -582,15 +625,13 @@ __device__ __forceinline__ auto pingpong_odd_barrier(const Ctx& c, char* smem, i
   };
 }
 
-template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong(
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int SYNC>
+__device__ __forceinline__ void attn_fwd_pingpong_tile(const Ctx& c, char* smem,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int q_mode) {
   using T = Tile<D, NW, BN, QT, 2>;
   static_assert(NW % 2 == 0, "two wave groups");
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
 
   bf16x8 qf[QT][D / 16];
   load_q<D, QT>(Q + c.head, c.q0w, N, q_mode, qf, c.lane);
@@ -622,14 +663,14 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
     sched_mfma_with_reads<(D / 16) * (BN / 32), 1, QT, kPfQK>();
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] softmax | [t=2j+1] pv(j) from V slot 0, qk(j+1) from K slot 1
-      block_barrier();
+      if constexpr (SYNC == 2) block_barrier();
       pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j, s, pb, o, m_run, ms_run, l_run, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 1, copy);
       }
       if (j + 1 < n) {  // block j+1 (odd): slots swap
-        block_barrier();
+        if constexpr (SYNC == 2) block_barrier();
         pingpong_valu_turn<D, BN, QT, CAUSAL, 0>(c, j + 1, s, pb, o, m_run, ms_run, l_run, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j + 1, off, qf, s, pb, o, 1, copy);
@@ -639,14 +680,14 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
   } else {
     for (int j = 0; j < n; j += 2) {
       // block j (even): [t=2j] pv(j-1) from V slot 1, qk(j) from K slot 0 | [t=2j+1] softmax
-      block_barrier();
+      if constexpr (SYNC == 2) block_barrier();
       pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 1, 0>(c, smem, j - 1, off, qf, s, pb, o, 0, no_copy);
       {
         auto copy = pingpong_odd_barrier<D, NW, BN, 0>(c, smem, j);
         pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j, s, pb, o, m_run, ms_run, l_run, copy);
       }
       if (j + 1 < n) {
-        block_barrier();
+        if constexpr (SYNC == 2) block_barrier();
         pingpong_mfma_turn<D, NW, BN, QT, CAUSAL, 0, 1>(c, smem, j, off, qf, s, pb, o, 0, no_copy);
         auto copy = pingpong_odd_barrier<D, NW, BN, 1>(c, smem, j + 1);
         pingpong_valu_turn<D, BN, QT, CAUSAL, 2 * LD>(c, j + 1, s, pb, o, m_run, ms_run, l_run, copy);
@@ -660,6 +701,27 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, ms_run, l_run, c.c_log2, c.lane);
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int SYNC>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int q_mode) {
+  using T = Tile<D, NW, BN, QT, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  if constexpr (!CAUSAL) {
+    Ctx c;
+    make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, 0, c);
+    attn_fwd_pingpong_tile<D, NW, BN, QT, CAUSAL, OCC, SYNC>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+      Ctx c;
+      if (!make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, pass, c)) break;
+      if (pass > 0) block_barrier();  // every wave is done with the ring of the previous tile
+      attn_fwd_pingpong_tile<D, NW, BN, QT, CAUSAL, OCC, SYNC>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fused ping-pong kernel
@@ -720,7 +782,7 @@ __device__ __forceinline__ void pp_fused_matrix_turn(char* smem, int jp, int nw,
 }
 
 template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int PRE>
-__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong_fused(
+__device__ __forceinline__ void attn_fwd_pingpong_fused_tile(const Ctx& c, char* smem,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int n_qtiles, float c_log2, int q_mode) {
@@ -728,8 +790,6 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
   static_assert(NW % 2 == 0, "two wave groups");
   constexpr int NPRE = PRE ? 2 : 0;
   constexpr int LD = Tile<D, NW, BN>::LOADS;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
-  const Ctx c = make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2);
   const int nw = (c.kv_end_w + BN - 1) / BN;  // this wave's live blocks (wave-uniform)
 
   bf16x8 qf[QT][D / 16];
@@ -821,6 +881,27 @@ __global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   store_rows<D, QT>(O, LSE, c.head, c.bh, N, c.qi0, o, m_run, ms_run, l_run, c.c_log2, c.lane);
+}
+
+template <int D, int NW, int BN, int QT, bool CAUSAL, int OCC, int PRE>
+__global__ __launch_bounds__(NW * 64, (NW * OCC + 3) / 4) void attn_fwd_pingpong_fused(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
+    int n_qtiles, float c_log2, int q_mode) {
+  using T = Tile<D, NW, BN, QT, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  if constexpr (!CAUSAL) {
+    Ctx c;
+    make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, 0, c);
+    attn_fwd_pingpong_fused_tile<D, NW, BN, QT, CAUSAL, OCC, PRE>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+      Ctx c;
+      if (!make_ctx<D, T::BM, BN, 32 * QT, CAUSAL>(K, V, N, n_qtiles, c_log2, pass, c)) break;
+      if (pass > 0) block_barrier();  // every wave is done with the ring of the previous tile
+      attn_fwd_pingpong_fused_tile<D, NW, BN, QT, CAUSAL, OCC, PRE>(c, smem, Q, K, V, O, LSE, N, n_qtiles, c_log2, q_mode);
+    }
+  }
 }
 
 }  // namespace

@@ -37,7 +37,7 @@ namespace {
 
 using attn_fwd_impl::Variant;
 
-enum Schedule { kSimple = 0, kPipelined = 1, kPingPong = 2, kPingPongFused = 3, kPingPongPre = 4 };
+enum Schedule { kSimple = 0, kPipelined = 1, kPingPong = 2, kPingPongFused = 3, kPingPongPre = 4, kPingPong1 = 5 };
 
 // Launch one variant; the scale reaches the kernel as scale_args gives it.
 template <int D, int NW, int BN, int QT, int SCHED, int ST, int OCC = 1>
@@ -45,17 +45,19 @@ hipError_t launch(const void* q, const void* k, const void* v, float* out, float
                   int H, int N, int causal, float scale, hipStream_t stream) {
   using T = Tile<D, NW, BN, QT, ST>;
   const int n_qt = (N + T::BM - 1) / T::BM;
-  const long long G = (long long)B * H * n_qt;
+  const long long G = fwd_grid((long long)B * H, n_qt, causal);
   const ScaleArgs sa = scale_args(scale);
   const float c = sa.c_log2;
   const int neg = sa.q_mode;
   const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
+  clear_last_hip_error();
   const dim3 grid((unsigned)G), block(NW * 64);
-  if constexpr (SCHED == kPingPong) {
+  if constexpr (SCHED == kPingPong || SCHED == kPingPong1) {
+    constexpr int SYNC = SCHED == kPingPong ? 2 : 1;
     if (causal)
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, true, OCC, SYNC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
     else
-      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false, OCC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
+      hipLaunchKernelGGL((attn_fwd_pingpong<D, NW, BN, QT, false, OCC, SYNC>), grid, block, 0, stream, qq, kk, vv, out, lse, N, n_qt, c, neg);
   } else if constexpr (SCHED == kPingPongFused || SCHED == kPingPongPre) {
     constexpr int PRE = SCHED == kPingPongPre;
     if (causal)

@@ -203,6 +203,7 @@ int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_c
   const int nc = (S + L - 1) / L;
   const long long parts = (L + kCsRows - 1) / kCsRows;
   if (groups * parts > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  clear_last_hip_error();
   hipLaunchKernelGGL((chunk_scan_fwd<4, kCsRows / 128>), dim3((unsigned)(groups * parts)), dim3(256), 0,
                      (hipStream_t)stream,
                      (const uint16_t*)x, (const uint16_t*)cb, dt, dA_cumsum, out, S, H, L, nc);

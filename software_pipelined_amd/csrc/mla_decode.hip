@@ -281,6 +281,7 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   if (workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
   float* ws_o = (float*)workspace;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * kMlaDv;
+  clear_last_hip_error();
   hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)p.groups, (unsigned)p.nc), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
                      scale_args(scale).q_mode);

@@ -236,6 +236,19 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
         a.attn_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 0, 1.0, None)
 
 
+def test_library_shares_torchs_hip_runtime(attn):
+    """Loading the library in a fresh process leaves exactly one HIP runtime
+    mapped: the library must bind torch's, whose pointers and streams it is
+    handed (with two runtimes every launch fails)."""
+    code = ("from software_pipelined_amd import attn; attn.load_library(); "
+            "print('\\n'.join(sorted({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l})))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    runtimes = r.stdout.split()
+    assert len(runtimes) == 1, runtimes
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
