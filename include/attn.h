@@ -43,8 +43,10 @@ enum attn_status {
                               except lse (and the backward's lse), 4 bytes       */
   ATTN_ERR_HIP = 6,        /* the HIP runtime reported an error at launch         */
   /* 7 is not used */
-  ATTN_ERR_WORKSPACE = 8   /* decoding, backward, MLA decoding: workspace smaller
+  ATTN_ERR_WORKSPACE = 8,  /* decoding, backward, MLA decoding: workspace smaller
                               than the entry's workspace-size function reports  */
+  ATTN_ERR_TOO_LARGE = 9   /* attn_fwd_decode_static: the shape needs more scratch
+                              than attn_decode_static_max_bytes()               */
 };
 
 /*
@@ -137,6 +139,24 @@ int attn_decode_workspace_size(int B, int H, int Nq, int Nkv, int d, size_t* byt
 int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
                     int Nq, int Nkv, int d, float scale, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * attn_fwd_decode_static -- attn_fwd_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation, arguments and kernels without the
+ * workspace. The chunk partials go to a fixed device array of
+ * attn_decode_static_max_bytes() bytes (16 MiB) inside the library, one per
+ * GPU, held until the process ends; the entry calls no allocator. A shape
+ * whose attn_decode_workspace_size exceeds that returns ATTN_ERR_TOO_LARGE
+ * before any HIP call. The array is looked up for the current device on the
+ * first call there (hipGetSymbolAddress; make the stream's device current).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller. No part of the array needs clearing between calls.
+ */
+size_t attn_decode_static_max_bytes(void);
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
+                           int Nq, int Nkv, int d, float scale, void* stream);
 
 /*
  * Attention backward (the backward pass the Twill software-pipelining

@@ -28,6 +28,7 @@ ATTN_ERR_BAD_SCALE = 4
 ATTN_ERR_MISALIGNED = 5
 ATTN_ERR_HIP = 6
 ATTN_ERR_WORKSPACE = 8
+ATTN_ERR_TOO_LARGE = 9
 
 _lib = None
 
@@ -87,6 +88,11 @@ def load_library():
     lib.attn_fwd_decode.restype = ctypes.c_int
     lib.attn_fwd_decode.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_decode_static_max_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_static_max_bytes.argtypes = []
+    lib.attn_fwd_decode_static.restype = ctypes.c_int
+    lib.attn_fwd_decode_static.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -141,6 +147,16 @@ def attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, workspace, works
     """Same arguments as the C ``attn_fwd_decode``: device pointers (ints), sizes, stream."""
     return load_library().attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, float(scale),
                                           workspace, workspace_bytes, stream)
+
+
+def attn_decode_static_max_bytes() -> int:
+    return load_library().attn_decode_static_max_bytes()
+
+
+def attn_fwd_decode_static(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, stream) -> int:
+    """Same arguments as the C ``attn_fwd_decode_static`` (no workspace: the
+    library's fixed per-GPU scratch holds the chunk partials)."""
+    return load_library().attn_fwd_decode_static(q, k, v, out, lse, B, H, Nq, Nkv, d, float(scale), stream)
 
 
 # ------------------------------------------------------------ torch convenience

@@ -2,6 +2,8 @@
 //
 // Part of libattn.so; the C ABI is declared in include/attn.h.
 
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace {
@@ -256,7 +258,34 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
   return hipGetLastError();
 }
 
-// Argument checks of the decoding entry (before any HIP call).
+// ---------------------------------------------------------------- no-allocation entry
+// attn_fwd_decode_static keeps the chunk partials in this fixed device array
+// instead of a caller workspace, for callers that cannot allocate. Each GPU
+// the library runs on holds its own copy until the process ends. In host
+// code the array's name is not a device address: the address of the current
+// device's copy comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of scratch (looked up on its first use).
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// Argument checks shared by both decoding entries (before any HIP call).
 int decode_check(const DecodePlan& p, const void* q, const void* k, const void* v, const float* out,
                  const float* lse, float scale) {
   uint32_t sbits;
@@ -302,6 +331,23 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, float* out, flo
   if (workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
   const hipError_t e = launch_decode_d(d, p, q, k, v, out, lse, B * H, Nq, Nkv, scale, workspace,
                                        (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_decode_static_max_bytes(void) { return kDecodeScratchBytes; }
+
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, float* out, float* lse, int B, int H,
+                           int Nq, int Nkv, int d, float scale, void* stream) {
+  DecodePlan p;
+  int st = decode_plan(B, H, Nq, Nkv, d, &p);
+  if (st != ATTN_OK) return st;
+  st = decode_check(p, q, k, v, out, lse, scale);
+  if (st != ATTN_OK || p.rows == 0) return st;
+  if (p.ws_bytes > kDecodeScratchBytes) return ATTN_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != ATTN_OK) return st;
+  const hipError_t e = launch_decode_d(d, p, q, k, v, out, lse, B * H, Nq, Nkv, scale, ws, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -143,6 +143,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_MISALIGNED: return "pointer misaligned (16 bytes; 4 for lse and the backward's per-row statistics)";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than the entry point's workspace-size function reports";
+    case ATTN_ERR_TOO_LARGE: return "shape needs more scratch than the no-allocation entry's fixed buffer holds";
     default: return "unknown status";
   }
 }

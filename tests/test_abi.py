@@ -213,7 +213,7 @@ def test_status_codes_match_the_header(attn):
     # entries that take one
     assert codes == {"ATTN_OK": 0, "ATTN_ERR_NULL_PTR": 1, "ATTN_ERR_BAD_SHAPE": 2, "ATTN_ERR_HEAD_DIM": 3,
                      "ATTN_ERR_BAD_SCALE": 4, "ATTN_ERR_MISALIGNED": 5, "ATTN_ERR_HIP": 6,
-                     "ATTN_ERR_WORKSPACE": 8}
+                     "ATTN_ERR_WORKSPACE": 8, "ATTN_ERR_TOO_LARGE": 9}
     for name, value in codes.items():
         assert getattr(attn, name) == value, name
     assert not hasattr(attn, "ATTN_ERR_BAD_VARIANT")
