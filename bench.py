@@ -578,6 +578,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--gemm-ref", type=int, default=0,
+                    help="instead of attention, time torch's bf16 matmul of two M x M matrices "
+                         "(hipBLASLt): the practical MFMA ceiling on the same card and clock")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -600,6 +603,30 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_step": n * 4, "steps": args.warmup + args.steps}), flush=True)
+        return
+
+    if args.gemm_ref:
+        # library GEMM reference for the MFMA roofline: same card, same power
+        # and clock limits as the attention kernels; not part of the product
+        assert torch.cuda.is_available(), "bench needs a HIP device"
+        m = args.gemm_ref
+        g = torch.Generator(device="cuda:0").manual_seed(7)
+        a = torch.randn((m, m), device="cuda:0", generator=g).to(torch.bfloat16)
+        b = torch.randn((m, m), device="cuda:0", generator=g).to(torch.bfloat16)
+        c = torch.empty((m, m), device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(args.warmup):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b, out=c)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        tf = 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_ref": f"torch.matmul bf16 {m}x{m}x{m}", "ms_per_call": round(ms, 4),
+                          "tflops": round(tf, 1), "frac_of_2500": round(tf / 2500.0, 4)}), flush=True)
         return
 
     if not os.path.exists(attn.LIB_PATH):

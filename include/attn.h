@@ -172,7 +172,7 @@ int attn_fwd_decode_static(const void* q, const void* k, const void* v, float* o
  *   out, lse      : device, float32, the attn_fwd outputs for the same q, k,
  *                   v, causal and scale ([B][H][N][d] and [B][H][N])
  *   dq, dk, dv    : device, float32, [B][H][N][d]; fully overwritten
- *   d             : 64 or 128 (256 returns ATTN_ERR_HEAD_DIM)
+ *   d             : 64, 128 or 256
  *   causal, scale : as for attn_fwd
  *   workspace, workspace_bytes : device scratch owned by the caller, 16-byte
  *                   aligned, at least attn_bwd_workspace_size bytes (else

@@ -108,6 +108,11 @@ __device__ __forceinline__ int opaque_lane() {
   return v;
 }
 
+// Workgroups per CU the main kernels are compiled for: two waves per SIMD
+// (256 registers each) at d = 64 and 128; one at d = 256, where a wave's
+// K/V (or Q/dO) operands and its two d-wide accumulators need about 450.
+constexpr int bwd_blocks_per_cu(int D, int NW) { return D == 256 ? 4 / NW : 8 / NW; }
+
 // One 256-byte statistics block into a wave's own 1 KiB LDS slot (lanes past
 // the block read zeros).
 __device__ __forceinline__ void issue_stat_copy(const float* src, char* dst) {
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const float* __restrict__ O
 //   P = exp2(c*S - log2e*LSE), dS = P (dP - D)   (accumulator layout: query rows)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = transposed reads, B = P / dS in bf16)
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
+__global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dK,
     float* __restrict__ dV, int N, int n_ktiles, float c_log2, int q_mode, float scale) {
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dkdv(
 //   dS^T = exp2(c*S^T - log2e*LSE) (dP^T - D)   (masked keys: 0)
 //   dQ^T += K^T dS^T                (A = transposed reads of the K image)
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
+__global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ stats, float* __restrict__ dQ, int N,
     int n_qtiles, float c_log2, int q_mode, float scale) {
@@ -355,7 +360,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bwd_dq(
   }
 }
 
-// Backward: two waves per SIMD in both main kernels; 64-key blocks in the dQ
+// Backward: two waves per SIMD in both main kernels (one at d = 256,
+// bwd_blocks_per_cu); 64-key blocks in the dQ
 // kernel, 32-row query blocks in the dK/dV kernel; 32 keys or queries per
 // wave. The dQ kernel runs 4 waves per workgroup. The dK/dV kernel runs 8 at
 // d = 128 when that still leaves at least four workgroups per CU (each
@@ -375,7 +381,7 @@ struct BwdPlan {
 
 int bwd_plan(int B, int H, int N, int d, BwdPlan* p) {
   if (B < 0 || H < 0 || N < 0) return ATTN_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEAD_DIM;
   long long bh = 0, rows = 0, elems = 0;
   if (__builtin_mul_overflow((long long)B, (long long)H, &bh) || __builtin_mul_overflow(bh, (long long)N, &rows) ||
       __builtin_mul_overflow(rows, (long long)d, &elems) || elems > (1LL << 50))
@@ -385,7 +391,7 @@ int bwd_plan(int B, int H, int N, int d, BwdPlan* p) {
   p->kw = d == 128 && bh * ((N + 255) / 256) >= 4LL * kBwdCUs ? 8 : 4;
   p->n_ktiles = (N + 32 * p->kw - 1) / (32 * p->kw);
   p->n_qtiles = (N + 32 * kBwdQWaves - 1) / (32 * kBwdQWaves);
-  if (bh * p->nqb > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  if (!grid_fits(bh * p->nqb, 512)) return ATTN_ERR_BAD_SHAPE;  // the largest of the three grids
   p->ws_bytes = (size_t)bh * p->nqb * kBwdStatBytes;
   return ATTN_OK;
 }
@@ -410,7 +416,7 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
     hipLaunchKernelGGL((attn_bwd_dkdv<D, D == 128 ? 8 : 4, CAUSAL>), dim3(gk), dim3(512), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                        (const float*)stats, dk, dv, N, p.n_ktiles, c, neg, scale);
-  else
+  else  // 4 waves: d = 64, d = 256, and d = 128 on small grids
     hipLaunchKernelGGL((attn_bwd_dkdv<D, 4, CAUSAL>), dim3(gk), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                        (const float*)stats, dk, dv, N, p.n_ktiles, c, neg, scale);
@@ -451,9 +457,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* out, cons
   if (d == 64)
     e = causal ? launch_bwd<64, true>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm)
                : launch_bwd<64, false>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm);
-  else
+  else if (d == 128)
     e = causal ? launch_bwd<128, true>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm)
                : launch_bwd<128, false>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm);
+  else
+    e = causal ? launch_bwd<256, true>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm)
+               : launch_bwd<256, false>(p, q, k, v, out, lse, dout, dq, dk, dv, N, scale, workspace, sm);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

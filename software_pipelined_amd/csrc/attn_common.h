@@ -630,6 +630,10 @@ __device__ __forceinline__ bool make_ctx(const uint16_t* K, const uint16_t* V, i
 }
 
 // Workgroups in the grid of a forward launch (see make_ctx).
+// A dispatch counts its work-items in 32 bits: workgroups times threads per
+// workgroup must stay below 2^32 (shapes beyond that are ATTN_ERR_BAD_SHAPE).
+inline bool grid_fits(long long workgroups, int threads) { return workgroups <= 0xFFFFFFFFLL / threads; }
+
 __host__ __device__ inline long long fwd_grid(long long BH, int n_qtiles, int causal) {
   return BH * (causal ? (n_qtiles + 1) / 2 : n_qtiles);
 }

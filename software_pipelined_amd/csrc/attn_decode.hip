@@ -224,7 +224,7 @@ int decode_plan(int B, int H, int Nq, int Nkv, int d, DecodePlan* p) {
   if (rows == 0) return ATTN_OK;
   if (Nkv < 1) return ATTN_ERR_BAD_SHAPE;  // a query with no key has no softmax
   const long long groups = bh * p->n_qt;
-  if (elems_q > (1LL << 50) || elems_kv > (1LL << 50) || groups > INT_MAX || rows > INT_MAX)
+  if (elems_q > (1LL << 50) || elems_kv > (1LL << 50) || !grid_fits(groups, 256) || !grid_fits(rows, 256))
     return ATTN_ERR_BAD_SHAPE;
   const long long nblk = (Nkv + kDecodeBN - 1) / kDecodeBN;
   const long long waves = decode_waves(d, p->nw);

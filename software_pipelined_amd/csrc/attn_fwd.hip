@@ -99,7 +99,8 @@ int validate(const void* q, const void* k, const void* v, const float* out, cons
     return ATTN_ERR_BAD_SHAPE;
   if (rows == 0) return ATTN_OK;
   // element offsets are 64-bit in the kernel; the grid is one dimension
-  if (elems > (1LL << 50) || grid > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  // (a dispatch counts work-items in 32 bits: workgroups x 512 threads < 2^32)
+  if (elems > (1LL << 50) || grid > 0xFFFFFFFFLL / 512) return ATTN_ERR_BAD_SHAPE;
   if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_PTR;
   const uintptr_t m = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
   if ((m & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_MISALIGNED;

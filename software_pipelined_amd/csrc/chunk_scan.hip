@@ -202,7 +202,7 @@ int chunk_scan(const void* x, const void* cb, const float* dt, const float* dA_c
   if ((m & 15) != 0) return ATTN_ERR_MISALIGNED;
   const int nc = (S + L - 1) / L;
   const long long parts = (L + kCsRows - 1) / kCsRows;
-  if (groups * parts > INT_MAX) return ATTN_ERR_BAD_SHAPE;
+  if (!grid_fits(groups * parts, 256)) return ATTN_ERR_BAD_SHAPE;
   clear_last_hip_error();
   hipLaunchKernelGGL((chunk_scan_fwd<4, kCsRows / 128>), dim3((unsigned)(groups * parts)), dim3(256), 0,
                      (hipStream_t)stream,

@@ -105,7 +105,8 @@ def test_bwd_validation_happens_before_any_hip_call(attn):
     # 256 bytes of statistics per 32 query rows of each head
     assert st == attn.ATTN_OK and need == 2 * 16 * 32 * 256
     assert attn.attn_bwd_workspace_size(0, 16, 1000, 128) == (attn.ATTN_OK, 0)
-    assert attn.attn_bwd_workspace_size(1, 1, 1000, 256)[0] == attn.ATTN_ERR_HEAD_DIM
+    assert attn.attn_bwd_workspace_size(1, 1, 1000, 256) == (attn.ATTN_OK, 32 * 256)
+    assert attn.attn_bwd_workspace_size(1, 1, 1000, 96)[0] == attn.ATTN_ERR_HEAD_DIM
     assert attn.attn_bwd_workspace_size(1, -1, 1000, 64)[0] == attn.ATTN_ERR_BAD_SHAPE
     big = 1 << 30
     assert attn.attn_bwd_workspace_size(big, big, big, 64)[0] == attn.ATTN_ERR_BAD_SHAPE
@@ -119,7 +120,7 @@ def test_bwd_validation_happens_before_any_hip_call(attn):
     for name in ("q", "k", "v", "o", "l", "do", "dq", "dk", "dv"):
         assert call(**{name: 0}) == attn.ATTN_ERR_NULL_PTR, name
     assert call(ws=0) == attn.ATTN_ERR_NULL_PTR
-    assert call(d=256) == attn.ATTN_ERR_HEAD_DIM
+    assert call(d=96) == attn.ATTN_ERR_HEAD_DIM
     assert call(N=-1) == attn.ATTN_ERR_BAD_SHAPE
     for sc in (float("nan"), float("inf")):
         assert call(s=sc) == attn.ATTN_ERR_BAD_SCALE

@@ -89,6 +89,9 @@ SHAPES = [
     (1, 2, 384, 128, False),    # three full tiles
     (1, 1, 500, 128, True),
     (2, 2, 300, 64, False),
+    (1, 1, 1, 256, False),
+    (1, 2, 100, 256, True),     # d = 256: one wave per SIMD, ragged blocks
+    (2, 1, 300, 256, False),
 ]
 
 
@@ -174,6 +177,26 @@ def test_bwd_workload_d64_causal_8k_sampled(oracle_mod):
     krows = np.concatenate([h * cfg.N + I.sample_rows(1, 1, cfg.N, per_head=6, seed=52 + h) for h in heads])
     dq, dk, dv = oracle_mod.attn_bwd_rows(q, k, v, do, cfg.causal, cfg.scale, qrows, krows)
     compare_grads((got[0][qrows], got[1][krows], got[2][krows]), (dq, dk, dv), cfg.name)
+
+
+def test_bwd_workload_d256_causal_4k_sampled(oracle_mod):
+    """The causal N=4096 d=256 workload at full size: dQ on sampled query rows
+    of every head, dK and dV on sampled key rows of every head."""
+    cfg = I.CAUSAL_4K_D256
+    _say(f"case bwd workload {cfg.name}")
+    _sampled_parity(oracle_mod, cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, cfg.seed, tuple(range(cfg.B * cfg.H)),
+                    cfg.name)
+
+
+def test_bwd_d256_negative_scale(oracle_mod):
+    B, H, N, d = 1, 1, 160, 256
+    _say("case bwd d256 negative scale / stressed keys")
+    q, k, v = I.gen_qkv(B, H, N, d, seed=73, key_stress=True)
+    do = I.gen_dout(B, H, N, d, seed=73)
+    for causal in (False, True):
+        got = run_bwd(q, k, v, do, causal, np.float32(-0.0625))
+        ref = oracle_mod.attn_bwd(q, k, v, do, causal, np.float32(-0.0625))
+        compare_grads(got, ref, f"bwd d256 scale -0.0625 causal {causal}")
 
 
 def test_bwd_reuses_one_workspace(oracle_mod):
