@@ -40,7 +40,8 @@ def run_mla(q, kv, scale, workspace=None):
 SHAPES = [
     # (B, H, N)
     (1, 64, 1),        # one cache row
-    (1, 64, 33),       # a ragged second block
+    (1, 64, 33),       # one block, its second half holds one key
+    (1, 64, 96),       # the second half of the last block holds no key
     (2, 128, 100),
     (1, 128, 1000),    # several blocks per chunk, ragged tail
     (3, 64, 2049),
