@@ -19,19 +19,20 @@ namespace {
 // workgroup per (b, chunk, h): 4 waves, wave w owns chunk rows 64w .. 64w+63;
 // every input of a 32-step block (x, the cb columns, dt, dA_cumsum) streams
 // through a two-slot LDS ring, so the next block's loads are in flight while
-// this one is computed. Workgroup ids run over heads fastest, so the heads
-// sharing one cb chunk run together.
+// this one is computed. Logical workgroup ids run over heads fastest and
+// stay on one XCD in runs (xcd_remap), so the heads sharing one cb chunk run
+// together on one L2.
 constexpr int kCsP = 64;   // channels per head
 constexpr int kCsBK = 32;  // steps per block
 // One ring slot: the x block (32 x 64 bf16, V layout), the cb columns of the
-// block for all 256 possible rows (64 bytes per row, 16-byte chunks XORed
-// with (row >> 1) & 3), then dt and dA_cumsum of the block's 32 steps (one
-// 1 KiB copy each, only the first 128 bytes used).
+// block for the workgroup's rows (64 bytes per row, 16-byte chunks XORed with
+// (row >> 1) & 3), then dt and dA_cumsum of the block's 32 steps (128 bytes
+// each, copied by 8 lanes).
 constexpr int kCsX = kCsBK * kCsP * 2;
 template <int RW>
 struct CsSlot {
   static constexpr int CB = RW * kCsBK * 2;    // cb columns of the block for the workgroup's RW rows
-  static constexpr int BYTES = kCsX + CB + 2 * 1024;
+  static constexpr int BYTES = kCsX + CB + 2 * 128;
 };
 
 
@@ -66,8 +67,10 @@ __device__ __forceinline__ void cs_copy_block(const uint16_t* xh, const uint16_t
   if (wave == 0) {  // dt and dA_cumsum of the block's 32 steps
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(dtc + k0), (short)0, 128, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(dac + k0), (short)0, 128, kRsrcWord3);
-    cs_dma(rd, lane * 16, slot + kCsX + CsSlot<RW>::CB);
-    cs_dma(ra, lane * 16, slot + kCsX + CsSlot<RW>::CB + 1024);
+    if (lane < 8) {  // 128 bytes each: the other lanes would only write zeros
+      cs_dma(rd, lane * 16, slot + kCsX + CsSlot<RW>::CB);
+      cs_dma(ra, lane * 16, slot + kCsX + CsSlot<RW>::CB + 128);
+    }
   }
 }
 
@@ -84,8 +87,11 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nparts = (L + RW - 1) / RW;
-  const int h = blockIdx.x % H, part = (blockIdx.x / H) % nparts, c = (blockIdx.x / (H * nparts)) % nc,
-            b = blockIdx.x / (H * nparts * nc);
+  // logical id: heads fastest, then parts, chunks, sequences; xcd_remap keeps
+  // consecutive ids on one XCD, so the heads (and parts) of one chunk share
+  // that XCD's L2 copy of the chunk's cb
+  const int L_id = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = L_id % H, part = (L_id / H) % nparts, c = (L_id / (H * nparts)) % nc, b = L_id / (H * nparts * nc);
   const int c0 = c * L, Lc = min(L, S - c0), r0 = part * RW;
   if (r0 >= Lc) return;  // workgroup-uniform: this part of a short last chunk is empty
   const int nblk = (min(Lc, r0 + RW) + kCsBK - 1) / kCsBK;
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         dtv[hf][e] = *(LDS_AS const f32x4*)(dts + (16 * hf + 8 * e + 4 * hl) * 4);
-        dav[hf][e] = *(LDS_AS const f32x4*)(dts + 1024 + (16 * hf + 8 * e + 4 * hl) * 4);
+        dav[hf][e] = *(LDS_AS const f32x4*)(dts + 128 + (16 * hf + 8 * e + 4 * hl) * 4);
       }
     bf16x8 pb[QT][2];
 #pragma unroll
