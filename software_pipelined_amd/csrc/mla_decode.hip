@@ -175,8 +175,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     const int slot = (j - b0) & 1;
     wait_vmcnt<kMlaTouch>();
     block_barrier();
-    mla_copy_block(kvb, min(j + 1, b1 - 1) * kMlaBN, N, smem + (slot ^ 1) * kMlaBlock, wave, lane);
-    mla_touch_block(kvb, min(j + 2, b1 - 1) * kMlaBN, N, dummy, wave, lane);
+    // the next block's 18 copies are spread over this block's 68 MFMAs (9 in
+    // the QK stream, 9 in the PV stream): issued together they hold the wave
+    // at the texture unit for about a fifth of the block
+    const __amdgpu_buffer_rsrc_t rnext = mla_rsrc(kvb, min(j + 1, b1 - 1) * kMlaBN, N);
+    char* cdst = smem + (slot ^ 1) * kMlaBlock;
     const char* Ks = smem + slot * kMlaBlock;
     const int kv0 = j * kMlaBN + 32 * half;
     f32x16 s[1][1];
@@ -194,11 +197,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
           const int kn = kk + kMlaPfQK;
           kf[kk % kMlaPfQK] = *(LDS_AS const bf16x8*)(Ks + kq[kn & 3] + 128 * (kn >> 2));
         }
+        if ((kk & 3) == 3) mla_copy_one(rnext, kk >> 2, cdst, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
       s[0][0] = s2[0] + s2[1];
       if (kv0 + 32 > N) mask_block<32, 1, false>(s, kv0, 0, N, lane);
     } else {
+#pragma unroll
+      for (int t = 0; t < 9; ++t) mla_copy_one(rnext, t, cdst, wave, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[0][0][r] = -INFINITY;
     }
@@ -230,19 +236,32 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     pt[1][0] = *(LDS_AS const bf16x8*)(xp_other);
     pt[1][1] = *(LDS_AS const bf16x8*)(xp_other + 64 * 16);
     rescale_block<256, 1>(o, alpha);
+    // PV step i = 16 kt + 8 p + t: O^T tile t += V^T(key tile kt, rows 16p..) P^T;
+    // the transposed reads run kMlaPfPV steps ahead, and copies 9-17 of the
+    // next block go out at steps 1, 5, .., 29 and 31
+    auto tr_read = [&](int i, i16x4& a0, i16x4& a1) {
+      const int kt = i >> 4, p = (i >> 3) & 1, t = i & 7;
+      const int base = 128 * (t >> 1) + (kt ? vrow_other : vrow_mine) + (16 * p) * kMlaRow;
+      a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][0]));
+      a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][1]));
+    };
+    i16x4 va[kMlaPfPV][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int i = 0; i < kMlaPfPV; ++i) tr_read(i, va[i][0], va[i][1]);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int base = 128 * (t >> 1) + (kt ? vrow_other : vrow_mine) + (16 * p) * kMlaRow;
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][0]));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][1]));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[kt][p], o[0][t], 0, 0, 0);
-        }
-    sched_mfma_with_reads<32, 2, 1, kMlaPfPV>();
+    for (int i = 0; i < 32; ++i) {
+      const int kt = i >> 4, p = (i >> 3) & 1, t = i & 7;
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[i % kMlaPfPV][0], va[i % kMlaPfPV][1], 0, 1, 2, 3, 4,
+                                                             5, 6, 7));
+      o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[kt][p], o[0][t], 0, 0, 0);
+      if (i + kMlaPfPV < 32) tr_read(i + kMlaPfPV, va[i % kMlaPfPV][0], va[i % kMlaPfPV][1]);
+      if ((i & 3) == 1 || i == 31) mla_copy_one(rnext, i == 31 ? 17 : 9 + (i >> 2), cdst, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // issued after every copy of the next block, so that at the top of the
+    // next block only these kMlaTouch reads may still be in flight
+    mla_touch_block(kvb, min(j + 2, b1 - 1) * kMlaBN, N, dummy, wave, lane);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   // the row sum: this wave's keys, then the partner's (same alpha sequence)
