@@ -289,9 +289,57 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
   if (half == 0 && hl == 0) ws_lse[(size_t)c * rows + row] = kLn2 * (m_run[0] + __builtin_amdgcn_logf(l_tot));
 }
 
-// Merge of the NC chunk partials of one (b, h) row (as attn_decode_combine,
-// two output dims per thread).
-__global__ __launch_bounds__(256, 1) void mla_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+// Merge of the NC chunk partials of one (b, h) row, for NC <= kMlaMergePF
+// (many rows, few chunks): one wave per row, four rows per workgroup, lane l owning output dims 8l .. 8l + 7. Every lane reads
+// all NC chunk LSEs (the same addresses in every lane: one request each) and
+// its 8 dims of every partial, all issued before any weight is known, so the
+// merge costs one memory round trip; no barrier. (Few rows with many chunks
+// go to mla_combine_wide instead.) Weights and sums run over the
+// chunks in order: w_c = exp(LSE_c - max), O = sum w_c O_c / sum w_c,
+// LSE = max + ln(sum w_c) (an empty chunk has LSE -inf and weight 0).
+constexpr int kMlaMergePF = 8;  // chunks whose partials are loaded up front
+__global__ __launch_bounds__(256) void mla_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+                                                   float* __restrict__ O, float* __restrict__ LSE, int rows, int nc) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  f32x4 p0[kMlaMergePF], p1[kMlaMergePF];
+  float lse[kMlaMergePF];
+#pragma unroll
+  for (int c = 0; c < kMlaMergePF; ++c) {
+    // past the last chunk: a duplicate of it (an L2 hit), never weighted;
+    // guarding the loads instead makes the compiler keep every slot live
+    const int cc = min(c, nc - 1);
+    const float* src = ws_o + ((size_t)cc * rows + row) * kMlaDv + 8 * lane;
+    p0[c] = *(const f32x4*)src;
+    p1[c] = *(const f32x4*)(src + 4);
+    lse[c] = ws_lse[(size_t)cc * rows + row];
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kMlaMergePF; ++c)
+    if (c < nc) mx = fmaxf(mx, lse[c]);
+  float wsum = 0.f;
+  f32x4 a0 = f32x4{}, a1 = f32x4{};
+#pragma unroll
+  for (int c = 0; c < kMlaMergePF; ++c)
+    if (c < nc) {
+      const float w = __builtin_amdgcn_exp2f((lse[c] - mx) * kLog2e);  // 0 for an empty chunk
+      wsum += w;
+      a0 += w * p0[c];
+      a1 += w * p1[c];
+    }
+  const float inv = 1.0f / wsum;
+  float* dst = O + (size_t)row * kMlaDv + 8 * lane;
+  *(f32x4*)dst = a0 * inv;
+  *(f32x4*)(dst + 4) = a1 * inv;
+  if (lane == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
+}
+
+// Merge for many chunks (more than kMlaMergePF): one workgroup per row (as
+// attn_decode_combine), two output dims per thread, the chunk weights shared
+// through LDS.
+__global__ __launch_bounds__(256, 1) void mla_combine_wide(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                      float* __restrict__ O, float* __restrict__ LSE, int rows, int nc) {
   __shared__ float w_sh[kDecodeMaxChunks];
   __shared__ float red[8];
@@ -342,6 +390,7 @@ __global__ __launch_bounds__(256, 1) void mla_combine(const float* __restrict__ 
   O[(size_t)row * kMlaDv + tid + 256] = a1 / wsum;
   if (tid == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
 }
+
 
 // MLA decoding: H a multiple of 64 (64 heads per workgroup); chunks sized so
 // that one resident round of workgroups (one per CU) covers the cache, at
@@ -408,8 +457,12 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)(p.groups * p.nc)), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
                      scale_args(scale).q_mode);
-  hipLaunchKernelGGL(mla_combine, dim3((unsigned)p.rows), dim3(256), 0, (hipStream_t)stream, (const float*)ws_o,
-                     (const float*)ws_lse, out, lse, (int)p.rows, p.nc);
+  if (p.nc <= kMlaMergePF)
+    hipLaunchKernelGGL(mla_combine, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
+                       (const float*)ws_o, (const float*)ws_lse, out, lse, (int)p.rows, p.nc);
+  else
+    hipLaunchKernelGGL(mla_combine_wide, dim3((unsigned)p.rows), dim3(256), 0, (hipStream_t)stream,
+                       (const float*)ws_o, (const float*)ws_lse, out, lse, (int)p.rows, p.nc);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
