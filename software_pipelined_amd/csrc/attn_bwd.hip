@@ -369,13 +369,18 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dq
 // traffic: -10% time at N = 16384), else 4 (more, smaller workgroups balance
 // short causal grids better); at d = 64 a 32-row block is too small to split
 // over 8 waves.
-constexpr int kBwdQWaves = 4;
+// dQ kernel waves: 8 at d = 128 without the mask (256 queries per
+// workgroup, so every K/V block staged in LDS serves twice as many queries:
+// -1.2 % time at N = 16384); else 4 (d = 64 keeps three 4-wave workgroups
+// per CU, which 8-wave ones would cut to one: +7 % time; causal grids are
+// neutral; d = 256 fits one wave per SIMD only).
+constexpr int bwd_q_waves(int d, bool causal) { return d == 128 && !causal ? 8 : 4; }
 constexpr int kBwdCUs = 256;
 constexpr int kBwdBN = 64;
 
 struct BwdPlan {
   long long bh;
-  int nqb, kw, n_ktiles, n_qtiles;
+  int nqb, kw, qw, n_ktiles, n_qtiles;
   size_t ws_bytes;  // statistics: bh * nqb * 256 bytes
 };
 
@@ -390,7 +395,8 @@ int bwd_plan(int B, int H, int N, int d, BwdPlan* p) {
   p->nqb = (N + kBwdRows - 1) / kBwdRows;
   p->kw = d == 128 && bh * ((N + 255) / 256) >= 4LL * kBwdCUs ? 8 : 4;
   p->n_ktiles = (N + 32 * p->kw - 1) / (32 * p->kw);
-  p->n_qtiles = (N + 32 * kBwdQWaves - 1) / (32 * kBwdQWaves);
+  p->qw = bwd_q_waves(d, false);  // attn_bwd sets the mask's value
+  p->n_qtiles = (N + 32 * p->qw - 1) / (32 * p->qw);
   if (!grid_fits(bh * p->nqb, 512)) return ATTN_ERR_BAD_SHAPE;  // the largest of the three grids
   p->ws_bytes = (size_t)bh * p->nqb * kBwdStatBytes;
   return ATTN_OK;
@@ -420,7 +426,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
     hipLaunchKernelGGL((attn_bwd_dkdv<D, 4, CAUSAL>), dim3(gk), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                        (const float*)stats, dk, dv, N, p.n_ktiles, c, neg, scale);
-  hipLaunchKernelGGL((attn_bwd_dq<D, kBwdQWaves, kBwdBN, CAUSAL>), dim3(gq), dim3(kBwdQWaves * 64), 0, stream,
+  constexpr int QW = bwd_q_waves(D, CAUSAL);
+  hipLaunchKernelGGL((attn_bwd_dq<D, QW, kBwdBN, CAUSAL>), dim3(gq), dim3(QW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
                      (const float*)stats, dq, N, p.n_qtiles, c, neg, scale);
   return hipGetLastError();
@@ -452,6 +459,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* out, cons
                       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace;
   if ((m & 15) != 0 || ((uintptr_t)lse & 3) != 0) return ATTN_ERR_MISALIGNED;
   if (workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+  p.qw = bwd_q_waves(d, causal != 0);
+  p.n_qtiles = (N + 32 * p.qw - 1) / (32 * p.qw);
   hipError_t e;
   const hipStream_t sm = (hipStream_t)stream;
   if (d == 64)
