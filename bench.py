@@ -608,6 +608,10 @@ def main():
     from software_pipelined_amd import attn, build as hip_build, inputs
 
     if args.copy_mib:
+        # plain device copies: the counter calibration (fp32 -> fp32, as many
+        # bytes read as written) and the practical HBM rates of the card for
+        # that mix and for one byte read per two written (bf16 -> fp32, the
+        # ChunkScan mix); not part of the product
         assert torch.cuda.is_available(), "bench needs a HIP device"
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -615,7 +619,21 @@ def main():
         for _ in range(args.warmup + args.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_step": n * 4, "steps": args.warmup + args.steps}), flush=True)
+        rates = {}
+        src16 = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        for name, a, nbytes in (("fp32_copy", src, 8 * n), ("bf16_to_fp32", src16, 6 * n)):
+            for _ in range(args.warmup):
+                dst.copy_(a)
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(args.steps):
+                dst.copy_(a)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / args.steps
+            rates[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        print(json.dumps({"copy_bytes_per_step": n * 4, "steps": args.warmup + args.steps, "rates": rates}),
+              flush=True)
         return
 
     if args.gemm_ref:

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
   static_assert(NW == 4, "one 1 KiB copy per wave covers a 32 x 64 bf16 block");
   constexpr int RW = 32 * QT * NW;
   constexpr int SLOT = CsSlot<RW>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
+  // the ring, reused at the end to stage each wave's 32 output rows
+  __shared__ __attribute__((aligned(1024))) char smem[std::max(2 * SLOT, NW * 32 * kCsP * 4)];
+  static_assert(QT == 1, "one staged 32-row image per wave");
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nparts = (L + RW - 1) / RW;
@@ -161,17 +163,39 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_fwd(const uint16_t* __rest
     pv_block<kCsP, kCsBK, QT>(slot, off, pb, o);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+  // Output rows through LDS, so that each store instruction writes four whole
+  // 256-byte rows: the accumulators hold, per lane, 4-channel groups of one
+  // row. All waves have finished with the ring before it is reused. Row r of
+  // a wave's 32 x 64 fp32 image keeps its 16-byte chunk c at c ^ (r & 15),
+  // so neither the row-wise writes nor the row-major reads conflict.
+  block_barrier();
+  char* stage = smem + wave * (32 * kCsP * 4);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int m = mw + 32 * qt + (lane & 31);
-    if (m < Lc) {
-      float* orow = OUT + (((size_t)b * S + c0 + m) * H + h) * kCsP;
+    const int r = lane & 31;
 #pragma unroll
-      for (int t = 0; t < kCsP / 32; ++t)
+    for (int t = 0; t < kCsP / 32; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(f32x4*)(orow + t * 32 + g * 8 + hl * 4) =
-              f32x4{o[qt][t][4 * g], o[qt][t][4 * g + 1], o[qt][t][4 * g + 2], o[qt][t][4 * g + 3]};
+      for (int g = 0; g < 4; ++g) {
+        const int c = (t * 32 + g * 8 + hl * 4) / 4;  // 16-byte chunk of the row
+        *(LDS_AS f32x4*)(stage + r * (kCsP * 4) + ((c ^ (r & 15)) << 4)) =
+            f32x4{o[qt][t][4 * g], o[qt][t][4 * g + 1], o[qt][t][4 * g + 2], o[qt][t][4 * g + 3]};
+      }
+    // the rows are read back by other lanes of the same wave: its LDS
+    // accesses complete in order; the fence keeps the compiler from moving
+    // the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int c = lane & 15;
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 4 * i + (lane >> 4);
+      v[i] = *(LDS_AS const f32x4*)(stage + rr * (kCsP * 4) + ((c ^ (rr & 15)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = mw + 32 * qt + 4 * i + (lane >> 4);
+      if (m < Lc) *(f32x4*)(OUT + (((size_t)b * S + c0 + m) * H + h) * kCsP + 4 * c) = v[i];
     }
   }
 }

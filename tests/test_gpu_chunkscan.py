@@ -114,6 +114,34 @@ def test_chunk_scan_b64_workload_sampled(oracle_mod):
     compare(got[rows], ref, cfg.name)
 
 
+@pytest.mark.parametrize("shape", [(4, 3000, 64, 64, 256), (2, 5000, 64, 64, 128)],
+                         ids=lambda s: "b%d_s%d_h%d_p%d_l%d" % s)
+def test_chunk_scan_mid_size_ragged(oracle_mod, shape):
+    """Mid-size batches (3,072 and 5,120 (b, chunk, h) groups, several
+    workgroups per CU in flight) with ragged last chunks (184 steps: a full
+    and a partial 128-row part; 8 steps). Sampled rows: every row of the last
+    chunk at both ends of the batch for three heads, the first and last rows
+    of each 128-row part, and random rows."""
+    B, S, H, P, L = shape
+    _say(f"case chunk_scan mid-size ragged {shape}")
+    x, cb, dt, dacs = I.gen_chunk_scan(B, S, H, P, L, seed=900 + S)
+    got = run_cs(x, cb, dt, dacs, L).reshape(-1, P)
+    nc = (S + L - 1) // L
+    rng = np.random.default_rng(S)
+    rows = set(int(r) for r in rng.choice(B * S * H, size=4000, replace=False))
+    for b in (0, B - 1):
+        for s in range((nc - 1) * L, S):
+            for h in (0, H // 2, H - 1):
+                rows.add((b * S + s) * H + h)
+        for c in range(nc):
+            for m in (0, 127, 128, L - 1):
+                if c * L + m < S:
+                    rows.add((b * S + c * L + m) * H + (c % H))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = oracle_mod.chunk_scan_rows(x, cb, dt, dacs, L, rows)
+    compare(got[rows], ref, f"chunk_scan {shape}")
+
+
 def test_chunk_scan_is_deterministic():
     x, cb, dt, dacs = I.gen_chunk_scan(2, 700, 4, 64, 256, seed=5)
     a = run_cs(x, cb, dt, dacs, 256)
