@@ -270,23 +270,35 @@ def chunkscan_cpu_baseline(cfg, x, cb, dt, dacs, target_s: float):
     threads = attn_oracle.max_threads()
     rng = np.random.default_rng(12345)
     total_rows = cfg.B * cfg.S * cfg.H
-    # size the sample from a timed calibration, twice (the first timing carries
-    # one-off costs that would undersize it), for about target_s of work
+    # grow a timed sample until it takes an eighth of target_s (small samples
+    # cost more per row), then size the run for about target_s: one seeded
+    # sample of rows, or whole passes over every row when they all take less
     n = min(total_rows, 64 * threads)
-    for _ in range(2):
-        calib = np.sort(rng.choice(total_rows, size=n, replace=False))
+    while True:
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False))
         t0 = time.perf_counter()
-        attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, calib, threads=threads)
+        attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows, threads=threads)
         dt_s = max(time.perf_counter() - t0, 1e-6)
-        n = int(min(total_rows, max(threads, calib.size * min(target_s, 10 * dt_s) / dt_s)))
-    n = int(min(total_rows, max(threads, calib.size * target_s / dt_s)))
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+        if dt_s >= target_s / 8 or n == total_rows:
+            break
+        n = min(total_rows, n * 8)
+    rows_per_s = n / dt_s
+    passes = 1
+    if total_rows / rows_per_s < target_s:
+        n, passes = total_rows, max(1, int(round(target_s * rows_per_s / total_rows)))
+        rows = None
+    else:
+        n = int(target_s * rows_per_s)
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
-    attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows, threads=threads)
+    for _ in range(passes):
+        attn_oracle.chunk_scan_rows(x, cb, dt, dacs, cfg.L, rows, threads=threads)
     dt_s = time.perf_counter() - t0
-    nbytes = cfg.hbm_bytes() * n / total_rows
+    nbytes = cfg.hbm_bytes() * n / total_rows * passes
+    what = (f"all {total_rows} output rows, {passes} passes" if rows is None else
+            f"{n} of {total_rows} output rows (seeded uniform sample)")
     return {"value": nbytes / dt_s / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle", **host_cpu(),
-            "sample": f"{n} of {total_rows} output rows (seeded uniform sample), fp64 C oracle, {dt_s:.1f} s wall"}
+            "sample": f"{what}, fp64 C oracle, {dt_s:.1f} s wall"}
 
 
 def chunkscan_bench(args):
