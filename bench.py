@@ -525,13 +525,17 @@ def decode_bench(args):
     dq, dk, dv = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (q, k, v))
     out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.d), dtype=torch.float32, device=dev)
     lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device=dev)
-    st, need = attn.attn_decode_workspace_size(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d)
+    # grouped K/V heads: the G query heads of a group are adjacent in q, out
+    # and lse, so the call takes Hkv heads of G * Nq query rows
+    G = cfg.H // cfg.kv_heads
+    Hc, Nqc = cfg.kv_heads, G * cfg.Nq
+    st, need = attn.attn_decode_workspace_size(cfg.B, Hc, Nqc, cfg.Nkv, cfg.d)
     if st != 0:
         raise attn.AttnError(st)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(device=dev)
     args_c = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), lse.data_ptr(),
-              cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, float(cfg.scale), ws.data_ptr(), ws.numel(),
+              cfg.B, Hc, Nqc, cfg.Nkv, cfg.d, float(cfg.scale), ws.data_ptr(), ws.numel(),
               stream.cuda_stream)
 
     def step():
@@ -560,14 +564,15 @@ def decode_bench(args):
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a row sample")
-        cpu = decode_cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+        cpu = decode_cpu_baseline(cfg, q.reshape(cfg.B, Hc, Nqc, cfg.d), k, v, args.cpu_seconds)
     print(json.dumps({
         "metric": "split-KV decode: compulsory HBM bytes per second (q, k, v read once; out, lse written)",
         "value": round(nbytes * args.steps / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Nq": cfg.Nq, "Nkv": cfg.Nkv, "d": cfg.d,
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Hkv": cfg.kv_heads, "Nq": cfg.Nq,
+                   "Nkv": cfg.Nkv, "d": cfg.d,
                    "bytes_per_step": nbytes, "flops_per_step": cfg.flops(), "workspace_bytes": need},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,

@@ -129,6 +129,13 @@ int attn_fwd_variant(int id, const void* q, const void* k, const void* v, float*
  *             entry do not matter and are overwritten
  *   stream  : hipStream_t (NULL = default stream); two kernels are enqueued
  *
+ * Grouped K/V heads (G query heads sharing one K/V head, as in the LLAMA3
+ * models): with k, v of Hkv = H / G heads, [B][Hkv][Nkv][d], query head h
+ * reads K/V head h / G. The G query heads of a group are adjacent in q, out
+ * and lse, so that operation is exactly this call with H replaced by Hkv and
+ * Nq by G * Nq, on the same five buffers (and a workspace sized for that
+ * shape); each K/V head is then read once per group.
+ *
  * Same ownership, validation and asynchrony rules as attn_fwd; the library
  * allocates nothing. Calls sharing one workspace must not overlap.
  *

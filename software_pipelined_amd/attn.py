@@ -406,11 +406,14 @@ def attn_forward(q, k, v, causal: bool = False, scale=None, out=None, lse=None, 
 def attn_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=None):
     """Split-KV decoding on torch tensors already on the GPU.
 
-    q: bfloat16 [B, H, Nq, d]; k, v: bfloat16 [B, H, Nkv, d], contiguous.
-    Every query sees every key. Returns (out float32 [B, H, Nq, d], lse
-    float32 [B, H, Nq]); out, lse and the workspace (a uint8 tensor of at least
-    ``attn_decode_workspace_size`` bytes) are allocated with torch when not
-    given. Enqueued on ``stream`` (default: torch's current stream).
+    q: bfloat16 [B, H, Nq, d]; k, v: bfloat16 [B, Hkv, Nkv, d], contiguous,
+    with Hkv dividing H (Hkv < H: grouped K/V heads, query head h reading K/V
+    head h // (H / Hkv); the G = H / Hkv query heads of a group are adjacent
+    in q, so the C entry point is called with Hkv heads of G * Nq query rows
+    on the same buffers). Every query sees every key. Returns (out float32
+    [B, H, Nq, d], lse float32 [B, H, Nq]); out, lse and the workspace (a
+    uint8 tensor of at least ``attn_decode_workspace_size(B, Hkv, G * Nq, Nkv,
+    d)`` bytes) are allocated with torch when not given. Enqueued on ``stream`` (default: torch's current stream).
     """
     import torch
 
@@ -418,14 +421,15 @@ def attn_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError("q, k, v must be contiguous 4-d bfloat16 tensors on the GPU")
     B, H, Nq, d = q.shape
-    Nkv = k.shape[2]
-    if tuple(k.shape) != (B, H, Nkv, d) or k.shape != v.shape:
-        raise ValueError("k and v must be [B, H, Nkv, d] with q's B, H and d")
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if (tuple(k.shape) != (B, Hkv, Nkv, d) or k.shape != v.shape or Hkv < 1 or H % Hkv != 0):
+        raise ValueError("k and v must be [B, Hkv, Nkv, d] with q's B and d and Hkv dividing q's H")
+    G = H // Hkv  # query heads per K/V head: (H, Nq) -> (Hkv, G * Nq) over the same memory
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one GPU")
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
-    st, need = attn_decode_workspace_size(B, H, Nq, Nkv, d)
+    st, need = attn_decode_workspace_size(B, Hkv, G * Nq, Nkv, d)
     if st != ATTN_OK:
         raise AttnError(st)
     made = []
@@ -447,7 +451,7 @@ def attn_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=
         stream = torch.cuda.current_stream(q.device)
     _used_on(stream, *made)
     st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                         B, H, Nq, Nkv, d, scale, workspace.data_ptr(), ws_bytes,
+                         B, Hkv, G * Nq, Nkv, d, scale, workspace.data_ptr(), ws_bytes,
                          stream.cuda_stream)
     if st != ATTN_OK:
         raise AttnError(st)

@@ -114,26 +114,32 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
 
 // One workgroup per query row merges the row's NC chunk partials: the chunk
 // weights exp(LSE_c - max) are formed once in LDS, while each thread already
-// holds its first partials in registers; each thread sums one output
-// dimension over a slice of the chunks (coalesced across threads) and the
-// slices are added in LDS.
+// holds its first partials in registers. A thread owns four consecutive
+// output dimensions (16-byte loads) of one slice of the chunks: S = 1024 / D
+// slices, chunks c = slice + i S; the first 128 chunks of a row are loaded
+// before any weight is known, so up to 128 chunks cost one memory round
+// trip. The slices are added in LDS in a fixed order (deterministic).
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_lse,
                                                              float* __restrict__ O, float* __restrict__ LSE,
                                                              int rows, int nc) {
-  constexpr int G = 256 / D;  // chunk slices
+  constexpr int DG = D / 4;       // threads per slice (four dims each)
+  constexpr int S = 256 / DG;     // chunk slices: 16 at d = 64, 8 at d = 128, 4 at d = 256
+  constexpr int PF = 128 / S;     // partials per thread loaded before the weights are known
   __shared__ float w_sh[kDecodeMaxChunks];
-  __shared__ float red[256];
-  constexpr int PF = 32;      // partials per thread loaded before the weights are known
+  __shared__ f32x4 red4[S][DG];
+  __shared__ float red[8];
   const int tid = threadIdx.x, row = blockIdx.x;
-  const int dim = tid % D, g = tid / D;
-  float pre[PF];
+  const int g = tid % DG, sl = tid / DG;
+  const float* base = ws_o + (size_t)row * D + 4 * g;  // chunk c at base + c * rows * D
+  const size_t cstride = (size_t)rows * D;
+  f32x4 pre[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
-    const int c = g + i * G;
-    pre[i] = c < nc ? ws_o[((size_t)c * rows + row) * D + dim] : 0.f;
+    const int c = sl + i * S;
+    pre[i] = c < nc ? *(const f32x4*)(base + (size_t)c * cstride) : f32x4{};
   }
   float mx = -INFINITY;
   for (int c = tid; c < nc; c += 256) {
@@ -157,28 +163,31 @@ __global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __res
   if ((tid & 63) == 0) red[4 + (tid >> 6)] = ws;
   __syncthreads();  // also publishes every weight in w_sh
   const float wsum = (red[4] + red[5]) + (red[6] + red[7]);
-  float acc = 0.f;
+  f32x4 acc = {};
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
-    const int c = g + i * G;
+    const int c = sl + i * S;
     if (c < nc) acc += w_sh[c] * pre[i];
   }
-  int c = g + PF * G;
-  for (; c + 3 * G < nc; c += 4 * G) {
-    const float* src = ws_o + ((size_t)c * rows + row) * D + dim;
-    const size_t st = (size_t)G * rows * D;
-    acc += w_sh[c] * src[0] + w_sh[c + G] * src[st] + w_sh[c + 2 * G] * src[2 * st] +
-           w_sh[c + 3 * G] * src[3 * st];
+  int c = sl + PF * S;
+  for (; c + 3 * S < nc; c += 4 * S) {
+    const float* src = base + (size_t)c * cstride;
+    const size_t st = (size_t)S * cstride;
+    const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + st), d2 = *(const f32x4*)(src + 2 * st),
+                e = *(const f32x4*)(src + 3 * st);
+    acc += w_sh[c] * a;
+    acc += w_sh[c + S] * b;
+    acc += w_sh[c + 2 * S] * d2;
+    acc += w_sh[c + 3 * S] * e;
   }
-  for (; c < nc; c += G) acc += w_sh[c] * ws_o[((size_t)c * rows + row) * D + dim];
-  __syncthreads();  // every thread has read red[4..7]
-  red[tid] = acc;
+  for (; c < nc; c += S) acc += w_sh[c] * *(const f32x4*)(base + (size_t)c * cstride);
+  red4[sl][g] = acc;
   __syncthreads();
-  if (tid < D) {
-    float o = red[tid];
+  if (tid < DG) {
+    f32x4 o = red4[0][tid];
 #pragma unroll
-    for (int k = 1; k < G; ++k) o += red[tid + k * D];
-    O[(size_t)row * D + tid] = o / wsum;
+    for (int k = 1; k < S; ++k) o += red4[k][tid];
+    *(f32x4*)(O + (size_t)row * D + 4 * tid) = o / wsum;
   }
   if (tid == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
 }

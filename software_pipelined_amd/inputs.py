@@ -76,18 +76,25 @@ class DecodeConfig:
     Nkv: int
     d: int
     seed: int
+    Hkv: int = 0  # K/V heads, H / Hkv query heads per K/V head (0: one each)
 
     @property
     def scale(self) -> np.float32:
         return default_scale(self.d)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     def flops(self) -> int:
         """Algorithmic FLOPs: both contractions over all Nq x Nkv pairs."""
         return 4 * self.B * self.H * self.d * self.Nq * self.Nkv
 
     def kv_bytes(self) -> int:
-        """Compulsory HBM bytes: bf16 q, k, v read once; fp32 out and lse written."""
-        return (2 * self.B * self.H * (self.Nq + 2 * self.Nkv) * self.d
+        """Compulsory HBM bytes: bf16 q, k, v read once (each K/V head once,
+        whatever the number of query heads sharing it); fp32 out and lse
+        written."""
+        return (2 * self.B * (self.H * self.Nq + 2 * self.kv_heads * self.Nkv) * self.d
                 + 4 * self.B * self.H * self.Nq * (self.d + 1))
 
 
@@ -204,7 +211,10 @@ MLA_CONFIGS = [MLA_B1, MLA_B32]
 
 DECODE_B1 = DecodeConfig("decode_b1_h32_nq1_nkv4096_d128", 1, 32, 1, 4096, 128, seed=11)
 DECODE_B32 = DecodeConfig("decode_b32_h32_nq1_nkv4096_d128", 32, 32, 1, 4096, 128, seed=12)
-DECODE_CONFIGS = [DECODE_B1, DECODE_B32]
+# LLAMA3-8B's grouping: 32 query heads over 8 K/V heads
+DECODE_GQA_B1 = DecodeConfig("decode_b1_h32_kv8_nq1_nkv4096_d128", 1, 32, 1, 4096, 128, seed=13, Hkv=8)
+DECODE_GQA_B32 = DecodeConfig("decode_b32_h32_kv8_nq1_nkv4096_d128", 32, 32, 1, 4096, 128, seed=14, Hkv=8)
+DECODE_CONFIGS = [DECODE_B1, DECODE_B32, DECODE_GQA_B1, DECODE_GQA_B32]
 
 
 def default_scale(d: int) -> np.float32:
@@ -246,13 +256,15 @@ def gen_config(cfg: AttnConfig):
     return gen_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.key_stress)
 
 
-def gen_decode(B: int, H: int, Nq: int, Nkv: int, d: int, seed: int):
-    """Return (q [B, H, Nq, d], k [B, H, Nkv, d], v [B, H, Nkv, d]) as uint16
-    bf16 bits: Q, then K, then V drawn from one ``default_rng(seed)``."""
+def gen_decode(B: int, H: int, Nq: int, Nkv: int, d: int, seed: int, Hkv: int = 0):
+    """Return (q [B, H, Nq, d], k [B, Hkv, Nkv, d], v [B, Hkv, Nkv, d]) as
+    uint16 bf16 bits: Q, then K, then V drawn from one ``default_rng(seed)``
+    (Hkv = 0: one K/V head per query head)."""
+    hkv = Hkv or H
     rng = np.random.default_rng(seed)
     q = f32_to_bf16_bits(rng.standard_normal((B, H, Nq, d), dtype=np.float32))
-    k = f32_to_bf16_bits(rng.standard_normal((B, H, Nkv, d), dtype=np.float32))
-    v = f32_to_bf16_bits(rng.standard_normal((B, H, Nkv, d), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, hkv, Nkv, d), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, hkv, Nkv, d), dtype=np.float32))
     return q, k, v
 
 
@@ -272,7 +284,7 @@ def bwd_flops(cfg: AttnConfig) -> int:
 
 
 def gen_decode_config(cfg: DecodeConfig):
-    return gen_decode(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, cfg.seed)
+    return gen_decode(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, cfg.d, cfg.seed, cfg.Hkv)
 
 
 def sample_rows(B: int, H: int, N: int, per_head: int, seed: int, tile: int = 64) -> np.ndarray:

@@ -62,13 +62,42 @@ def test_decode_matches_oracle(oracle_mod, shape):
     _say(str(compare(out, lse, ro, rl, f"decode {shape}")))
 
 
+def oracle_grouped(oracle_mod, q, k, v, scale):
+    """The oracle's decoding with grouped K/V heads by their definition: each
+    K/V head repeated for the H / Hkv query heads that read it."""
+    G = q.shape[1] // k.shape[1]
+    return oracle_mod.attn_decode(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale)
+
+
 @pytest.mark.parametrize("cfg", I.DECODE_CONFIGS, ids=lambda c: c.name)
 def test_decode_workloads_all_rows(oracle_mod, cfg):
     _say(f"case decode workload {cfg.name}")
     q, k, v = I.gen_decode_config(cfg)
     out, lse = run_decode(q, k, v, cfg.scale)
-    ro, rl = oracle_mod.attn_decode(q, k, v, cfg.scale)
+    ro, rl = oracle_grouped(oracle_mod, q, k, v, cfg.scale)
     _say(str(compare(out, lse, ro, rl, cfg.name)))
+
+
+GROUPED = [
+    # (B, H, Hkv, Nq, Nkv, d)
+    (1, 4, 2, 1, 300, 128),    # two query heads per K/V head
+    (2, 8, 1, 2, 1000, 64),    # all heads on one K/V head, two query rows each
+    (1, 16, 4, 9, 257, 128),   # 36 query rows per K/V head: two query tiles
+    (1, 8, 2, 1, 4095, 256),
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED, ids=lambda s: "b%d_h%d_kv%d_nq%d_nkv%d_d%d" % s)
+def test_decode_grouped_kv_heads(oracle_mod, shape):
+    """Grouped K/V heads through the torch wrapper (one call over Hkv heads of
+    G * Nq query rows), against the oracle with each K/V head repeated."""
+    B, H, Hkv, Nq, Nkv, d = shape
+    _say(f"case decode grouped {shape}")
+    q, k, v = I.gen_decode(B, H, Nq, Nkv, d, seed=700 + sum(shape), Hkv=Hkv)
+    scale = I.default_scale(d)
+    out, lse = run_decode(q, k, v, scale)
+    ro, rl = oracle_grouped(oracle_mod, q, k, v, scale)
+    _say(str(compare(out, lse, ro, rl, f"decode grouped {shape}")))
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1, 100000, 64), (1, 8, 2, 131072, 128)],

@@ -309,10 +309,25 @@ def check_decode_uniform_and_constant(orc, lib=None):
                                rtol=1e-13, atol=1e-13)
 
 
+def check_decode_grouped_heads(orc, lib=None):
+    # Grouped K/V heads (G query heads per K/V head, query head h reading K/V
+    # head h // G) are, by definition, attention with each K/V head repeated G
+    # times; since a group's query heads are adjacent in memory, the same
+    # numbers come from the grouped-free call over Hkv heads of G * Nq rows
+    # (the reshape the decoding entry point documents), bit for bit
+    for (B, H, Hkv, Nq, Nkv, d) in [(2, 4, 2, 1, 9, 4), (1, 8, 1, 3, 5, 2), (1, 6, 3, 2, 17, 8)]:
+        G = H // Hkv
+        q, k, v = gen_decode(B, H, Nq, Nkv, d, seed=40 + H, Hkv=Hkv)
+        assert k.shape == (B, Hkv, Nkv, d)
+        ref_o, ref_l = orc.attn_decode(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.37, lib=lib)
+        o, l = orc.attn_decode(q.reshape(B, Hkv, G * Nq, d), k, v, 0.37, lib=lib)
+        assert np.array_equal(o.reshape(B, H, Nq, d), ref_o) and np.array_equal(l.reshape(B, H, Nq), ref_l)
+
+
 ALL_CHECKS = [check_closed_forms, check_mpmath, check_library, check_constant_v, check_causal_row0,
               check_zero_keys, check_lse_bounds, check_key_shift, check_permutations,
               check_causal_is_truncation, check_linear_in_v, check_dominant_key, check_row_subset,
-              check_decode_mpmath, check_decode_uniform_and_constant]
+              check_decode_mpmath, check_decode_uniform_and_constant, check_decode_grouped_heads]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
