@@ -155,6 +155,16 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const float* __restrict__ O
   }
 }
 
+// Issue priority of the MFMA phases (s_setprio) at d = 64, where the per-score
+// VALU work (exp2, the dS product, bf16 packing) is largest next to the MFMA
+// work: with two waves per SIMD the wave in its MFMA phase then issues ahead
+// of the other's VALU phase (same-host A/B: 3 % faster at d = 64; 1-3 %
+// slower at d = 128 and 256, which keep equal priority).
+template <int D, int P>
+__device__ __forceinline__ void bwd_prio() {
+  if constexpr (D == 64) __builtin_amdgcn_s_setprio(P);
+}
+
 // dK, dV. Workgroup = NW waves, wave w owns keys k0 + 32w .. +31 (K and V
 // rows as B-operand registers). Query blocks of 32 rows (Q, dO, statistics)
 // stream through a two-stage LDS ring. Per block and wave:
@@ -219,6 +229,7 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dk
     // fragments are read right before the MFMA that consumes them: with two
     // waves per SIMD the K/V operands and dK/dV accumulators leave little room
     f32x16 s = f32x16{}, dp = f32x16{};
+    bwd_prio<D, 1>();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(LDS_AS const bf16x8*)(Qs + bo.k(kk)), kf[0][kk], s, 0, 0, 0);
@@ -226,6 +237,7 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dk
     for (int kk = 0; kk < D / 16; ++kk)
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(LDS_AS const bf16x8*)(dOs + bo.k(kk)), vf[0][kk], dp, 0, 0, 0);
     const bool diag = CAUSAL && q0 < k0w + 31;
+    bwd_prio<D, 0>();
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 l2 = *(LDS_AS const f32x4*)(Ss + (8 * g + 4 * hl) * 4);
@@ -245,6 +257,7 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dk
     bf16x8 pb[1][2], dsb[1][2];
     softmax_pack<32, 1>(*(const f32x16(*)[1][1])&s, pb);
     softmax_pack<32, 1>(*(const f32x16(*)[1][1])&dp, dsb);
+    bwd_prio<D, 1>();
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -330,8 +343,10 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dq
     const char* Ks = smem + slot * STAGE;
     const char* Vs = Ks + MAT;
     f32x16 s[1][BN / 32], dp[1][BN / 32];
+    bwd_prio<D, 1>();
     qk_block_dual<D, BN>(Ks, bo, qf, s);
     qk_block_dual<D, BN>(Vs, bo, gf, dp);
+    bwd_prio<D, 0>();
     if (kv0 + BN > N || (CAUSAL && kv0 + BN - 1 > q0w)) mask_block<BN, 1, CAUSAL>(s, kv0, qi, N, lane);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -342,6 +357,7 @@ __global__ __launch_bounds__(NW * 64, bwd_blocks_per_cu(D, NW)) void attn_bwd_dq
       }
     bf16x8 dsb[1][BN / 16];
     softmax_pack<BN, 1>(s, dsb);
+    bwd_prio<D, 1>();
 #pragma unroll
     for (int p = 0; p < BN / 16; ++p)
 #pragma unroll
