@@ -614,8 +614,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus must be 1 "
-              "(multi-GPU sharding of (batch, head) pairs is described in DESIGN.md, not built)",
+        print("bench.py: the benchmark runs on one GPU; --gpus must be 1 "
+              "((batch, head) pairs would shard across GPUs with no exchange; that path is not built)",
               file=sys.stderr)
         sys.exit(2)
 
