@@ -83,6 +83,37 @@ def test_mla_negative_scale_and_reuse(oracle_mod):
         _say(str(compare(out, lse, ro, rl, f"mla {shape}")))
 
 
+@pytest.mark.parametrize("shape", [(1, 64, 65536), (64, 128, 512)], ids=lambda s: "b%d_h%d_n%d" % s)
+def test_mla_long_cache_and_many_rows(oracle_mod, shape):
+    """A 65,536-row cache for one sequence (256 chunks: the workgroup-per-row
+    merge) and 64 sequences of 128 heads over 512 rows (8,192 merged rows)."""
+    B, H, N = shape
+    _say(f"case mla {shape}")
+    q, kv = I.gen_mla(B, H, N, 576, seed=900 + B)
+    scale = np.float32(1.0 / np.sqrt(192.0))
+    out, lse = run_mla(q, kv, scale)
+    ro, rl = oracle_mod.mla_decode(q, kv, 512, scale)
+    _say(str(compare(out, lse, ro, rl, f"mla {shape}")))
+
+
+def test_mla_near_one_hot_rows(oracle_mod):
+    """The 64 rotary values (key only, not part of the value) of every
+    seventh cache row scaled by 16 (exact in bf16): those rows' scores grow
+    about 5x, so most heads put nearly all their weight on a few rows, the
+    case where rounding of P and of the partials matters most, while the
+    values keep unit scale (the bar is absolute)."""
+    B, H, N = 2, 128, 3000
+    _say(f"case mla stressed rows {(B, H, N)}")
+    q, kv = I.gen_mla(B, H, N, 576, seed=77)
+    kvf = I.bf16_bits_to_f32(kv)
+    kvf[:, ::7, 512:] *= np.float32(16.0)
+    kv = I.f32_to_bf16_bits(kvf)
+    scale = np.float32(1.0 / np.sqrt(192.0))
+    out, lse = run_mla(q, kv, scale)
+    ro, rl = oracle_mod.mla_decode(q, kv, 512, scale)
+    _say(str(compare(out, lse, ro, rl, "mla stressed rows")))
+
+
 def test_mla_is_deterministic():
     q, kv = I.gen_mla(2, 128, 1500, 576, seed=3)
     a = run_mla(q, kv, 0.07)
