@@ -608,6 +608,10 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--mfma-probe", choices=("reg", "lds"), default=None,
+                    help="instead of attention, time the library's matrix-core probe: a stream of bf16 "
+                         "MFMAs with register operands only (reg) or one 1 KiB LDS read per MFMA (lds), "
+                         "two workgroups of 4 waves per CU")
     ap.add_argument("--gemm-ref", type=int, default=0,
                     help="instead of attention, time torch's bf16 matmul of two M x M matrices "
                          "(hipBLASLt): the practical MFMA ceiling on the same card and clock")
@@ -651,6 +655,38 @@ def main():
             rates[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
         print(json.dumps({"copy_bytes_per_step": n * 4, "steps": args.warmup + args.steps, "rates": rates}),
               flush=True)
+        return
+
+    if args.mfma_probe:
+        # the sustained matrix-core rate for a plain MFMA stream, with and
+        # without LDS operand traffic, on the same card and clock as the
+        # attention kernels; not part of the product path
+        assert torch.cuda.is_available(), "bench needs a HIP device"
+        mode = 0 if args.mfma_probe == "reg" else 1
+        blocks, iters = 512, 4096
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+        stream = torch.cuda.Stream(device="cuda:0")
+
+        def probe():
+            st = attn.attn_probe_mfma(mode, blocks, iters, out.data_ptr(), stream.cuda_stream)
+            if st != 0:
+                raise attn.AttnError(st)
+
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            probe()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            probe()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        flops = blocks * 4 * iters * 16 * 32768
+        tf = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"mfma_probe": args.mfma_probe, "blocks": blocks, "iters": iters, "ms": round(ms, 4),
+                          "TFLOP/s": round(tf, 1), "frac_of_2500": round(tf / 2500.0, 4)}), flush=True)
         return
 
     if args.gemm_ref:

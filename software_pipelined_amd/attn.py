@@ -93,6 +93,8 @@ def load_library():
     lib.attn_fwd_decode_static.restype = ctypes.c_int
     lib.attn_fwd_decode_static.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
         ctypes.c_float, ctypes.c_void_p]
+    lib.attn_probe_mfma.restype = ctypes.c_int
+    lib.attn_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -147,6 +149,12 @@ def attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, scale, workspace, works
     """Same arguments as the C ``attn_fwd_decode``: device pointers (ints), sizes, stream."""
     return load_library().attn_fwd_decode(q, k, v, out, lse, B, H, Nq, Nkv, d, float(scale),
                                           workspace, workspace_bytes, stream)
+
+
+def attn_probe_mfma(mode, blocks, iters, out, stream) -> int:
+    """Same arguments as the C ``attn_probe_mfma`` (include/attn_probe.h): the
+    matrix-core stream used to measure the sustained MFMA rate and clock."""
+    return load_library().attn_probe_mfma(mode, blocks, iters, out, stream)
 
 
 def attn_decode_static_max_bytes() -> int:

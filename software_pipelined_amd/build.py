@@ -19,7 +19,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC_NAMES = ("attn_fwd.hip", "attn_fwd_d64.hip", "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_decode.hip",
-             "attn_bwd.hip", "chunk_scan.hip", "mla_decode.hip")
+             "attn_bwd.hip", "chunk_scan.hip", "mla_decode.hip", "clock_probe.hip")
 SRCS = [os.path.join(PKG, "csrc", f) for f in SRC_NAMES]
 LIB = os.path.join(PKG, "libattn.so")
 INCLUDE = os.path.join(ROOT, "include")

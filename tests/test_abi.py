@@ -1,5 +1,5 @@
 """CPU tests of the C ABI boundary: the library loads, exports every entry
-point declared in include/attn.h, and rejects bad arguments before any HIP
+point declared in include/*.h, and rejects bad arguments before any HIP
 call (so no GPU is needed). Also checks the build and bench host logic."""
 
 import os
@@ -11,6 +11,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,17 +24,33 @@ def attn():
     return a
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    """Names of the functions declared in the given headers (default: every
+    include/*.h), comments and preprocessor lines removed."""
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        text = "\n".join(line for line in text.splitlines() if not line.lstrip().startswith("#"))
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_strerror", "attn_num_variants", "attn_variant_name",
-              "attn_variant_info", "attn_default_variant", "attn_fwd_variant"):
-        assert n in names
+              "attn_variant_info", "attn_default_variant", "attn_fwd_variant", "attn_decode_workspace_size",
+              "attn_fwd_decode", "attn_decode_static_max_bytes", "attn_fwd_decode_static",
+              "attn_bwd_workspace_size", "attn_bwd", "chunk_scan", "mla_decode_workspace_size", "mla_decode",
+              "attn_probe_mfma"):
+        assert n in names, n
+
+
+def test_probe_validation_happens_before_any_hip_call(attn):
+    P = 1 << 20
+    assert attn.attn_probe_mfma(2, 1, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_probe_mfma(0, 0, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_probe_mfma(1, 1, 0, P, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_probe_mfma(0, 1, 1, 0, None) == attn.ATTN_ERR_NULL_PTR
 
 
 def test_library_exports_every_declared_symbol(attn):
