@@ -92,6 +92,9 @@ SHAPES = [
     (1, 1, 1, 256, False),
     (1, 2, 100, 256, True),     # d = 256: one wave per SIMD, ragged blocks
     (2, 1, 300, 256, False),
+    (1, 1, 1, 128, False),      # d = 128 without the mask (ping-pong dQ): one key block
+    (1, 3, 65, 128, False),     # two key blocks, the second holding one key
+    (2, 2, 1000, 128, False),   # 16 key blocks, ragged last block and query tile
 ]
 
 
