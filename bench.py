@@ -611,7 +611,8 @@ def main():
     ap.add_argument("--mfma-probe", choices=("reg", "lds"), default=None,
                     help="instead of attention, time the library's matrix-core probe: a stream of bf16 "
                          "MFMAs with register operands only (reg) or one 1 KiB LDS read per MFMA (lds), "
-                         "two workgroups of 4 waves per CU")
+                         "two workgroups of 4 waves per CU (--probe-blocks 256: one per CU, one wave per SIMD)")
+    ap.add_argument("--probe-blocks", type=int, default=512, help="workgroups of the matrix-core probe")
     ap.add_argument("--gemm-ref", type=int, default=0,
                     help="instead of attention, time torch's bf16 matmul of two M x M matrices "
                          "(hipBLASLt): the practical MFMA ceiling on the same card and clock")
@@ -663,7 +664,7 @@ def main():
         # attention kernels; not part of the product path
         assert torch.cuda.is_available(), "bench needs a HIP device"
         mode = 0 if args.mfma_probe == "reg" else 1
-        blocks, iters = 512, 4096
+        blocks, iters = args.probe_blocks, 4096
         out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
         stream = torch.cuda.Stream(device="cuda:0")
 
