@@ -608,10 +608,11 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device-to-device copy of this many "
                          "MiB per step (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--mfma-probe", choices=("reg", "lds"), default=None,
+    ap.add_argument("--mfma-probe", choices=("reg", "lds", "reg16", "lds16"), default=None,
                     help="instead of attention, time the library's matrix-core probe: a stream of bf16 "
-                         "MFMAs with register operands only (reg) or one 1 KiB LDS read per MFMA (lds), "
-                         "two workgroups of 4 waves per CU (--probe-blocks 256: one per CU, one wave per SIMD)")
+                         "32x32x16 MFMAs with register operands only (reg) or one 1 KiB LDS read per MFMA (lds), "
+                         "or of 16x16x32 MFMAs (reg16, lds16); two workgroups of 4 waves per CU "
+                         "(--probe-blocks 256: one per CU, one wave per SIMD)")
     ap.add_argument("--probe-blocks", type=int, default=512, help="workgroups of the matrix-core probe")
     ap.add_argument("--gemm-ref", type=int, default=0,
                     help="instead of attention, time torch's bf16 matmul of two M x M matrices "
@@ -663,7 +664,7 @@ def main():
         # without LDS operand traffic, on the same card and clock as the
         # attention kernels; not part of the product path
         assert torch.cuda.is_available(), "bench needs a HIP device"
-        mode = 0 if args.mfma_probe == "reg" else 1
+        mode = ("reg", "lds", "reg16", "lds16").index(args.mfma_probe)
         blocks, iters = args.probe_blocks, 4096
         out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
         stream = torch.cuda.Stream(device="cuda:0")
@@ -684,10 +685,12 @@ def main():
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / args.steps
-        flops = blocks * 4 * iters * 16 * 32768
+        flops = blocks * 4 * iters * 16 * (32768 if mode < 2 else 16384)
         tf = flops / (ms * 1e-3) / 1e12
+        lds_bytes = blocks * 4 * iters * 16 * 1024 if mode in (1, 3) else 0
         print(json.dumps({"mfma_probe": args.mfma_probe, "blocks": blocks, "iters": iters, "ms": round(ms, 4),
-                          "TFLOP/s": round(tf, 1), "frac_of_2500": round(tf / 2500.0, 4)}), flush=True)
+                          "TFLOP/s": round(tf, 1), "frac_of_2500": round(tf / 2500.0, 4),
+                          "lds_read_TB/s": round(lds_bytes / (ms * 1e-3) / 1e12, 2)}), flush=True)
         return
 
     if args.gemm_ref:

@@ -1,7 +1,7 @@
 // clock_probe.hip -- a measurement kernel of libattn.so: the matrix-core rate
-// and shader clock the card sustains for a stream of bf16 MFMAs, with the
-// operands in registers or with one 1 KiB LDS read per MFMA (the attention
-// kernels' ratio). Not part of any operator; the C ABI is declared in
+// and shader clock the card sustains for a stream of bf16 MFMAs (32x32x16 or
+// 16x16x32), with the operands in registers or with one 1 KiB LDS read per
+// MFMA. Not part of any operator; the C ABI is declared in
 // include/attn_probe.h.
 
 #include "attn_common.h"
@@ -13,13 +13,14 @@ constexpr int kProbeChains = 4;  // independent accumulators: back-to-back MFMA 
 constexpr int kProbeUnroll = 16;
 constexpr int kProbeLdsBytes = 64 * 1024;  // 16 KiB per wave: 16 distinct 1 KiB reads per pass
 
-// One workgroup of 4 waves (one per SIMD). Each wave runs iters x 16
-// v_mfma_f32_32x32x16_bf16 over kProbeChains accumulators; with LDS, every
-// MFMA's A operand is a fresh 16-byte-per-lane LDS read (1 KiB per wave;
-// the address moves with the iteration, so no read is loop-invariant),
-// issued 8 MFMAs ahead. The accumulators are summed and stored so that the
-// work cannot be dropped.
-template <bool LDS>
+// One workgroup of 4 waves (one per SIMD). Each wave runs iters x 16 MFMAs
+// (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_16x16x32_bf16 with SMALL: half
+// the work per instruction, same operand size) over kProbeChains
+// accumulators; with LDS, every MFMA's A operand is a fresh
+// 16-byte-per-lane LDS read (1 KiB per wave; the address moves with the
+// iteration, so no read is loop-invariant), issued 8 MFMAs ahead. The
+// accumulators are summed and stored so that the work cannot be dropped.
+template <bool LDS, bool SMALL>
 __global__ __launch_bounds__(256) void mfma_clock_probe(float* __restrict__ out, int iters) {
   __shared__ __attribute__((aligned(1024))) char smem[kProbeLdsBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -33,9 +34,16 @@ __global__ __launch_bounds__(256) void mfma_clock_probe(float* __restrict__ out,
   const float fa = (float)((lane & 3) - 1) * 0.0078125f, fb = (float)((lane >> 4) - 2) * 0.0078125f;
   const bf16x8 a0 = {(__bf16)fa, (__bf16)fb, (__bf16)fa, (__bf16)fb, (__bf16)fa, (__bf16)fb, (__bf16)fa, (__bf16)fb};
   const bf16x8 b0 = {(__bf16)fb, (__bf16)fa, (__bf16)fb, (__bf16)fa, (__bf16)fb, (__bf16)fa, (__bf16)fb, (__bf16)fa};
-  f32x16 acc[kProbeChains];
+  using acc_t = typename std::conditional<SMALL, f32x4, f32x16>::type;
+  acc_t acc[kProbeChains];
 #pragma unroll
-  for (int c = 0; c < kProbeChains; ++c) acc[c] = f32x16{};
+  for (int c = 0; c < kProbeChains; ++c) acc[c] = acc_t{};
+  auto mfma = [&](const bf16x8& a, acc_t& c) {
+    if constexpr (SMALL)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, c, 0, 0, 0);
+    else
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, c, 0, 0, 0);
+  };
   // each wave walks its own 16 KiB quarter of the LDS image, 1 KiB per read
   const char* base = smem + wave * (kProbeLdsBytes / 4) + lane * 16;
   for (int it = 0; it < iters; ++it) {
@@ -44,20 +52,18 @@ __global__ __launch_bounds__(256) void mfma_clock_probe(float* __restrict__ out,
 #pragma unroll
       for (int k = 0; k < kProbeUnroll; ++k) fr[k] = *(LDS_AS const bf16x8*)(base + (((k + it) & 15) << 10));
 #pragma unroll
-      for (int k = 0; k < kProbeUnroll; ++k)
-        acc[k % kProbeChains] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[k], b0, acc[k % kProbeChains], 0, 0, 0);
+      for (int k = 0; k < kProbeUnroll; ++k) mfma(fr[k], acc[k % kProbeChains]);
       sched_mfma_with_reads<kProbeUnroll, 1, 1, 8>();
     } else {
 #pragma unroll
-      for (int k = 0; k < kProbeUnroll; ++k)
-        acc[k % kProbeChains] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[k % kProbeChains], 0, 0, 0);
+      for (int k = 0; k < kProbeUnroll; ++k) mfma(a0, acc[k % kProbeChains]);
     }
   }
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kProbeChains; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += acc[c][r];
+    for (int r = 0; r < (SMALL ? 4 : 16); ++r) s += acc[c][r];
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -66,13 +72,16 @@ __global__ __launch_bounds__(256) void mfma_clock_probe(float* __restrict__ out,
 extern "C" {
 
 int attn_probe_mfma(int mode, int blocks, int iters, float* out, void* stream) {
-  if ((mode != 0 && mode != 1) || blocks < 1 || iters < 1 || blocks > (1 << 20)) return ATTN_ERR_BAD_SHAPE;
+  if (mode < 0 || mode > 3 || blocks < 1 || iters < 1 || blocks > (1 << 20)) return ATTN_ERR_BAD_SHAPE;
   if (!out) return ATTN_ERR_NULL_PTR;
   clear_last_hip_error();
-  if (mode == 0)
-    hipLaunchKernelGGL((mfma_clock_probe<false>), dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
-  else
-    hipLaunchKernelGGL((mfma_clock_probe<true>), dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((mfma_clock_probe<false, false>), dim3(blocks), dim3(256), 0, st, out, iters); break;
+    case 1: hipLaunchKernelGGL((mfma_clock_probe<true, false>), dim3(blocks), dim3(256), 0, st, out, iters); break;
+    case 2: hipLaunchKernelGGL((mfma_clock_probe<false, true>), dim3(blocks), dim3(256), 0, st, out, iters); break;
+    default: hipLaunchKernelGGL((mfma_clock_probe<true, true>), dim3(blocks), dim3(256), 0, st, out, iters); break;
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -47,7 +47,8 @@ def test_header_declares_the_entry_points():
 
 def test_probe_validation_happens_before_any_hip_call(attn):
     P = 1 << 20
-    assert attn.attn_probe_mfma(2, 1, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_probe_mfma(4, 1, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_probe_mfma(-1, 1, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
     assert attn.attn_probe_mfma(0, 0, 1, P, None) == attn.ATTN_ERR_BAD_SHAPE
     assert attn.attn_probe_mfma(1, 1, 0, P, None) == attn.ATTN_ERR_BAD_SHAPE
     assert attn.attn_probe_mfma(0, 1, 1, 0, None) == attn.ATTN_ERR_NULL_PTR
