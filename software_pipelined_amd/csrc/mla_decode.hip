@@ -17,59 +17,80 @@ namespace {
 // read from HBM once per 64 heads (and the H/64 workgroups of one chunk run
 // on one XCD, so the second finds the block in L2). One LDS image of a
 // 64-row block serves both S^T = K Q^T (row fragments) and O^T += V^T P^T
-// (transposed reads of its first 512 columns). Four waves: wave = 2*tile +
-// half takes the 32 heads of its tile; for S it takes rows [32 half, 32 half
-// + 32) of the block with the whole 576-wide contraction (its heads' Q^T
-// parked in AGPRs), for O^T the output dims [256 half, 256 half + 256) over
-// all 64 rows. The two waves of a tile agree on each block's max through LDS,
-// then swap their bf16 P^T halves: both hold the same softmax state.
+// (transposed reads of its first 512 columns). Eight waves, two per SIMD,
+// on v_mfma_f32_16x16x32_bf16 tiles of 16 heads: wave = 2*tile + half takes
+// the 16 heads of its tile; for S it takes rows [32 half, 32 half + 32) of
+// the block (two 16-key tiles) with the whole 576-wide contraction (its
+// heads' Q^T, 18 fragments, in registers), for O^T the output dims
+// [256 half, 256 half + 256) (16 tiles of 16) over all 64 rows. The two
+// waves of a tile agree on each block's max through LDS, then swap their
+// bf16 P^T halves: both hold the same softmax state.
+//
+// The P^T operand of the PV step is the S accumulator as it stands: lane l
+// holds keys 4g + i and 16 + 4g + i (g = l >> 4, i < 4) of its head l & 15,
+// which become contraction indices 8g + i and 8g + 4 + i of the 32-key step;
+// the V^T operand reads its rows in that same order (two transposed reads,
+// rows 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3).
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 constexpr int kMlaDk = 576, kMlaDv = 512, kMlaBN = 64;
-constexpr int kMlaRow = kMlaDk * 2;             // bytes per cache row
-constexpr int kMlaBlock = kMlaBN * kMlaRow;     // 72 KiB per 64-row block
-constexpr int kMlaCopies = kMlaBlock / 1024;    // 1 KiB copies per block (18 per wave)
-constexpr int kMlaK = kMlaDk / 16;              // 16-wide contraction steps (36)
-constexpr int kMlaST = 2;                       // ring slots: one block in flight behind the one in use
-constexpr int kMlaXP = 2 * 64 * 16;             // P^T exchange: two bf16x8 per lane
-constexpr int kMlaXchg = 4 * (kMlaXP + 64 * 4);  // per wave: P^T, and one float per lane (max, then l)
-constexpr int kMlaDummy = 4 * 256;                // L2-prefetch landing words, one per lane
-// fragment reads in flight ahead of the MFMAs (one wave per SIMD: nothing
-// else hides the LDS latency)
-constexpr int kMlaPfQK = 8, kMlaPfPV = 4;
+constexpr int kMlaWaves = 8;
+constexpr int kMlaRow = kMlaDk * 2;                // bytes per cache row
+constexpr int kMlaBlock = kMlaBN * kMlaRow;        // 72 KiB per 64-row block
+constexpr int kMlaCopies = kMlaBlock / 1024;       // 1 KiB copies per block
+constexpr int kMlaCpw = kMlaCopies / kMlaWaves;    // copies per wave and block (9)
+constexpr int kMlaK = kMlaDk / 32;                 // 32-wide contraction steps (18)
+constexpr int kMlaST = 2;                          // ring slots: one block in flight behind the one in use
+constexpr int kMlaXP = 64 * 16;                    // P^T exchange: one bf16x8 per lane
+constexpr int kMlaXchg = kMlaWaves * (kMlaXP + 64 * 4);  // per wave: P^T, and one float per lane (max, then l)
+constexpr int kMlaDummy = kMlaWaves * 256;         // L2-prefetch landing words, one per lane
+constexpr int kMlaSCopies = 7;                     // of a wave's 9 copies, those issued in the S stream
+// fragment reads in flight ahead of the MFMAs (a PV step takes two
+// transposed reads)
+constexpr int kMlaPfQK = 6, kMlaPfPV = 8;
 
-// 16-byte chunk c of row `row` sits at chunk (c & ~7) | ((c ^ f(row)) & 7),
-// f(row) = 4 ((row >> 1) & 1) + ((row >> 2) & 3): an XOR inside each group of
-// eight chunks (a row has 72), an involution. A row is 4.5 bank lines long,
-// so rows of one parity share bank halves; f takes all 8 values over the
-// even (and the odd) rows of any 16 consecutive rows (row-fragment reads
-// conflict-free), and rows b and b + 2 (b a multiple of 4) differ in bit 2
-// (the 4-row x 4-chunk transposed reads conflict-free).
-__device__ __forceinline__ int mla_swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int mla_phys(int c, int row) { return (c & ~7) | ((c ^ mla_swz(row)) & 7); }
+// 16-byte chunk c of row `row` sits at chunk c ^ f(row) (f < 8: an XOR
+// inside each group of eight chunks; a row has 72), with x = (row >> 1) & 7,
+// h = (x & 1) + 2 (((x >> 1) ^ (x >> 2)) & 1) and f = 2h + (x >> 2). A row is
+// 4.5 bank lines long, so rows of one parity share bank halves. f takes all
+// 8 values over the even (and over the odd) rows of any 16-aligned run of 16
+// rows (row-fragment reads: 16 rows x one chunk), and h all 4 values over
+// the even (odd) rows of rows 0-7, 8-15, {0-3, 8-11} and {4-7, 12-15} of such
+// a run (transposed reads: 8 rows x two adjacent chunks, under either
+// pairing of 16-lane groups). Both read kinds measure conflict-free on the
+// LDS counters; the plainer f = 2 ((row >> 1) & 3) + ((row >> 3) & 1), which
+// a 256-byte-pass bank model also finds conflict-free, costs the row-fragment
+// reads 4 conflict cycles each.
+__device__ __forceinline__ int mla_swz(int row) {
+  const int x = (row >> 1) & 7;
+  return 2 * ((x & 1) + 2 * (((x >> 1) ^ (x >> 2)) & 1)) + (x >> 2);
+}
+__device__ __forceinline__ int mla_phys(int c, int row) { return c ^ mla_swz(row); }
 
 // A block's rows [row0, min(row0 + 64, N)) as a buffer resource (reads past
-// them return zeros), and copy t (of 18 per wave) of the block into an LDS
-// image: 1 KiB per copy, lane l's 16 bytes at dst + 1024 (4t + wave) + 16 l.
+// them return zeros), and copy t (of 9 per wave) of the block into an LDS
+// image: 1 KiB per copy, lane l's 16 bytes at dst + 1024 (8t + wave) + 16 l.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mla_rsrc(const uint16_t* kvb, int row0, int N) {
   const int rows = __builtin_amdgcn_readfirstlane(min(N - row0, kMlaBN));
   return __builtin_amdgcn_make_buffer_rsrc((void*)(kvb + (size_t)row0 * kMlaDk), (short)0, rows * kMlaRow,
                                            kRsrcWord3);
 }
 __device__ __forceinline__ void mla_copy_one(__amdgpu_buffer_rsrc_t r, int t, char* dst, int wave, int lane) {
-  const int pidx = (t * 4 + wave) * 64 + lane;
+  const int idx = t * kMlaWaves + wave;
+  const int pidx = idx * 64 + lane;
   const int row = pidx / 72, pc = pidx % 72;
-  cs_dma(r, row * kMlaRow + (mla_phys(pc, row) << 4), dst + (t * 4 + wave) * 1024);
+  cs_dma(r, row * kMlaRow + (mla_phys(pc, row) << 4), dst + idx * 1024);
 }
 __device__ __forceinline__ void mla_copy_block(const uint16_t* kvb, int row0, int N, char* dst, int wave, int lane) {
   const __amdgpu_buffer_rsrc_t r = mla_rsrc(kvb, row0, N);
 #pragma unroll
-  for (int t = 0; t < kMlaCopies / 4; ++t) mla_copy_one(r, t, dst, wave, lane);
+  for (int t = 0; t < kMlaCpw; ++t) mla_copy_one(r, t, dst, wave, lane);
 }
 
 // L2 prefetch of a block: one 4-byte read per 64-byte line of its rows, each
 // landing in a throwaway LDS word of the wave (an LDS-bound load, so it ties
 // up no register). With one block in flight in the LDS ring, the copy of the
 // next block then finds its lines in L2 instead of waiting on HBM.
-constexpr int kMlaTouch = (kMlaBlock / 64 + 255) / 256;  // reads per wave per block (5)
+constexpr int kMlaTouch = (kMlaBlock / 64 + 64 * kMlaWaves - 1) / (64 * kMlaWaves);  // reads per wave per block (3)
 __device__ __forceinline__ void mla_touch_block(const uint16_t* kvb, int row0, int N, char* dummy, int wave,
                                                 int lane) {
   const int rows = __builtin_amdgcn_readfirstlane(min(N - row0, kMlaBN));
@@ -78,21 +99,33 @@ __device__ __forceinline__ void mla_touch_block(const uint16_t* kvb, int row0, i
   const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)dummy;
 #pragma unroll
   for (int t = 0; t < kMlaTouch; ++t) {
-    const int voff = ((t * 4 + wave) * 64 + lane) * 64;  // past the block: the range check reads nothing
+    const int voff = ((t * kMlaWaves + wave) * 64 + lane) * 64;  // past the block: the range check reads nothing
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
                  "s"(m0)
                  : "m0", "memory");
   }
 }
 
-// Grid: B * (H/64) * NC workgroups. Chunk c of the key blocks as chunk_begin.
-__global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
+// max and sum over lanes l and l ^ 16 (v_permlane16_swap exchanges the odd
+// 16-lane rows of one copy with the even rows of the other)
+__device__ __forceinline__ float swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Grid: B * (H/64) * NC workgroups of 512 threads. Chunk c of the key blocks
+// as chunk_begin.
+__global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
                                                             const uint16_t* __restrict__ KV,
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
                                                             int N, int H, int nc, float c_log2, int q_mode) {
-  static_assert(kMlaCopies % 4 == 0, "copies split evenly over four waves");
+  static_assert(kMlaCopies % kMlaWaves == 0, "copies split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg + kMlaDummy];
-  const int lane = threadIdx.x & 63, hl = lane >> 5, lq = lane & 31, ci = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = wave >> 1, half = wave & 1;
   // The H/64 head groups of one (sequence, chunk) take consecutive logical
@@ -101,162 +134,159 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
   const int hg = H / 64;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hgi = L % hg, bc = L / hg;
-  const int b = bc / nc, c = bc % nc, h0 = hgi * 64 + 32 * tile;
+  const int b = bc / nc, c = bc % nc, h0 = hgi * 64 + 16 * tile;
   const int nblk = (N + kMlaBN - 1) / kMlaBN;
   const int b0 = chunk_begin(c, nblk, nc), b1 = chunk_begin(c + 1, nblk, nc);
   const uint16_t* kvb = KV + (size_t)b * N * kMlaDk;
   const size_t rows = (size_t)(gridDim.x / (hg * nc)) * H;  // B * H
-  const size_t row = (size_t)b * H + h0 + lq;
+  const size_t row = (size_t)b * H + h0 + s16;               // this lane's head
+  float* obase = ws_o + ((size_t)c * rows + (size_t)b * H + h0) * kMlaDv + 256 * half;
 
   if (b0 == b1) {  // an empty chunk: weight zero in the merge
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(f32x4*)(ws_o + ((size_t)c * rows + row) * kMlaDv + 256 * half + t * 32 + g * 8 + hl * 4) = f32x4{};
-    if (half == 0 && hl == 0) ws_lse[(size_t)c * rows + row] = -INFINITY;
+    for (int h = 0; h < 16; ++h) *(f32x4*)(obase + (size_t)h * kMlaDv + 4 * lane) = f32x4{};
+    if (half == 0 && g == 0) ws_lse[(size_t)c * rows + row] = -INFINITY;
     return;
   }
   char* xbase = smem + kMlaST * kMlaBlock;
   char* xp_mine = xbase + wave * kMlaXP + lane * 16;
   const char* xp_other = xbase + (wave ^ 1) * kMlaXP + lane * 16;
-  float* xf_mine = (float*)(xbase + 4 * kMlaXP) + wave * 64 + lane;
-  const float* xf_other = (const float*)(xbase + 4 * kMlaXP) + (wave ^ 1) * 64 + lane;
-  // row-fragment offsets: row 32 half + lq, chunk 2kk + hl at
-  // 128 (kk >> 2) + 16 ((2 (kk & 3)) ^ hl ^ mla_swz(lq))  (mla_swz(32 m + lq) = mla_swz(lq))
-  const int e0 = hl ^ mla_swz(lq);
-  int kq[4];
+  float* xf_mine = (float*)(xbase + kMlaWaves * kMlaXP) + wave * 64 + lane;
+  const float* xf_other = (const float*)(xbase + kMlaWaves * kMlaXP) + (wave ^ 1) * 64 + lane;
+  char* dummy = xbase + kMlaXchg + wave * 256;
+  // row fragments (K and Q): row 16m + s16, chunk 4kk + g at
+  // 128 (kk >> 1) + 16 ((4 (kk & 1) + g) ^ f(s16))
+  const int fk = mla_swz(s16);
+  const int kq[2] = {s16 * kMlaRow + 16 * (g ^ fk), s16 * kMlaRow + 16 * ((4 + g) ^ fk)};
+  // transposed reads of dim tile t (dims 256 half + 16t ..): lane s16 of group
+  // g addresses row 4g + (s16 >> 2) (+16 for the second read) at dims
+  // 16t + 4 (s16 & 3): chunk 32 half + 8 (t >> 2) + ((2 (t & 3) + ((s16 >> 1) & 1)) ^ f(row))
+  const int r1 = 4 * g + (s16 >> 2), f1 = mla_swz(r1);
+  int vo[4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) kq[q4] = (32 * half + lq) * kMlaRow + 16 * ((2 * q4) ^ e0);
-  // transposed-read offsets (as LdsOffsets::v): rows r0 + 16p + 8r of a 32-row
-  // key tile, dims 256 half + 32t + 16g2 + 4(ci & 3); the swizzle of row
-  // r0 + 8r + 16p + 32kt is mla_swz(r0) ^ 2r (r0 < 8)
-  const int r0 = 4 * hl + (ci >> 2), c1 = 2 * ((lane >> 4) & 1) + ((ci & 3) >> 1);
-  const int tb = r0 * kMlaRow + 512 * half + 8 * (ci & 1), f0 = mla_swz(r0);
-  int to[2][2];  // [t & 1][r]
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    to[0][r] = tb + 16 * (c1 ^ f0 ^ (2 * r)) + 8 * r * kMlaRow;
-    to[1][r] = tb + 16 * ((4 ^ c1) ^ f0 ^ (2 * r)) + 8 * r * kMlaRow;
-  }
+  for (int u = 0; u < 4; ++u)
+    vo[u] = r1 * kMlaRow + 512 * half + 16 * ((2 * u + ((s16 >> 1) & 1)) ^ f1) + 8 * (s16 & 1);
   const int vrow_mine = 32 * half * kMlaRow, vrow_other = 32 * (half ^ 1) * kMlaRow;
 
-  f32x16 o[1][8];
+  f32x4 o[16];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[0][t] = f32x16{};
-  float m_run[1] = {-INFINITY}, l_run[1] = {0.f}, alpha[1];
+  for (int t = 0; t < 16; ++t) o[t] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
 
   // The 64 heads' Q rows are contiguous: they go to ring slot 1 as a 64-row
   // block (same layout) while block b0 goes to slot 0. Each iteration then
   // issues the next block's copies, and the L2 prefetch of the block after
   // (past the chunk end: duplicates of its last block, so the count of
   // younger loads at the top of a block is always kMlaTouch).
-  char* dummy = smem + kMlaST * kMlaBlock + kMlaXchg + wave * 256;
   mla_copy_block(Q + ((size_t)b * H + hgi * 64) * kMlaDk, 0, kMlaBN, smem + kMlaBlock, wave, lane);
   mla_copy_block(kvb, b0 * kMlaBN, N, smem, wave, lane);
   mla_touch_block(kvb, min(b0 + 1, b1 - 1) * kMlaBN, N, dummy, wave, lane);
-  wait_vmcnt<kMlaCopies / 4 + kMlaTouch>();  // the Q copies, issued first, have landed
+  wait_vmcnt<kMlaCpw + kMlaTouch>();  // the Q copies, issued first, have landed
   block_barrier();
-  // Q^T fragments (B operand): lane holds q[head h0 + lq][16 kk + 8 hl .. +7],
-  // row 32 tile + lq of the Q image; slot 1 is refilled only after the
+  // Q^T fragments (B operand): lane holds q[head h0 + s16][32 kk + 8g .. +7],
+  // row 16 tile + s16 of the Q image; slot 1 is refilled only after the
   // barrier at the top of the first block
   bf16x8 qf[1][kMlaK];
   {
-    const char* qimg = smem + kMlaBlock + (32 * tile - 32 * half) * kMlaRow;
+    const char* qimg = smem + kMlaBlock + 16 * tile * kMlaRow;
 #pragma unroll
     for (int kk = 0; kk < kMlaK; ++kk) {
-      u32x4 raw = *(LDS_AS const u32x4*)(qimg + kq[kk & 3] + 128 * (kk >> 2));
+      u32x4 raw = *(LDS_AS const u32x4*)(qimg + kq[kk & 1] + 128 * (kk >> 1));
       raw = apply_q_mode(raw, q_mode);
       qf[0][kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  park_in_agprs<1, kMlaK>(qf);
   for (int j = b0; j < b1; ++j) {
     const int slot = (j - b0) & 1;
     wait_vmcnt<kMlaTouch>();
     block_barrier();
-    // the next block's 18 copies are spread over this block's 68 MFMAs (9 in
-    // the QK stream, 9 in the PV stream): issued together they hold the wave
-    // at the texture unit for about a fifth of the block
+    // the next block's 9 copies are spread over this block's MFMA streams: 7
+    // in the S stream (one per 5 MFMAs), the last 2 early in the PV stream, so
+    // that they have most of a block to land
     const __amdgpu_buffer_rsrc_t rnext = mla_rsrc(kvb, min(j + 1, b1 - 1) * kMlaBN, N);
     char* cdst = smem + (slot ^ 1) * kMlaBlock;
-    const char* Ks = smem + slot * kMlaBlock;
+    const char* Vs = smem + slot * kMlaBlock;
+    const char* Ks = Vs + vrow_mine;
     const int kv0 = j * kMlaBN + 32 * half;
-    f32x16 s[1][1];
+    f32x4 s[2];
     if (kv0 < N) {  // wave-uniform: the second half of the last block may hold no key
-      // two accumulator chains (even and odd steps); fragments read
-      // kMlaPfQK steps ahead
-      f32x16 s2[2] = {f32x16{}, f32x16{}};
+      // step i = 2 kk + m: S tile m (keys 16m ..) += K(rows 16m.., k 32kk..) Q^T
+      s[0] = f32x4{};
+      s[1] = f32x4{};
+      auto kread = [&](int i) {
+        return *(LDS_AS const bf16x8*)(Ks + (i & 1) * 16 * kMlaRow + kq[(i >> 1) & 1] + 128 * (i >> 2));
+      };
       bf16x8 kf[kMlaPfQK];
 #pragma unroll
-      for (int i = 0; i < kMlaPfQK; ++i) kf[i] = *(LDS_AS const bf16x8*)(Ks + kq[i & 3] + 128 * (i >> 2));
+      for (int i = 0; i < kMlaPfQK; ++i) kf[i] = kread(i);
 #pragma unroll
-      for (int kk = 0; kk < kMlaK; ++kk) {
-        s2[kk & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kMlaPfQK], qf[0][kk], s2[kk & 1], 0, 0, 0);
-        if (kk + kMlaPfQK < kMlaK) {
-          const int kn = kk + kMlaPfQK;
-          kf[kk % kMlaPfQK] = *(LDS_AS const bf16x8*)(Ks + kq[kn & 3] + 128 * (kn >> 2));
-        }
-        if ((kk & 3) == 3) mla_copy_one(rnext, kk >> 2, cdst, wave, lane);
+      for (int i = 0; i < 2 * kMlaK; ++i) {
+        s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[i % kMlaPfQK], qf[0][i >> 1], s[i & 1], 0, 0, 0);
+        if (i + kMlaPfQK < 2 * kMlaK) kf[i % kMlaPfQK] = kread(i + kMlaPfQK);
+        if (i % 5 == 1) mla_copy_one(rnext, i / 5, cdst, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
-      s[0][0] = s2[0] + s2[1];
-      if (kv0 + 32 > N) mask_block<32, 1, false>(s, kv0, 0, N, lane);
+      if (kv0 + 32 > N) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[m][i] = (kv0 + 16 * m + 4 * g + i >= N) ? -INFINITY : s[m][i];
+      }
     } else {
 #pragma unroll
-      for (int t = 0; t < 9; ++t) mla_copy_one(rnext, t, cdst, wave, lane);
+      for (int t = 0; t < kMlaSCopies; ++t) mla_copy_one(rnext, t, cdst, wave, lane);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[0][0][r] = -INFINITY;
+      for (int m = 0; m < 2; ++m) s[m] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
     // the block max of each head over both halves (exact), then the common
     // running max; c > 0, so fl(max(s) c) = max(fl(s c))
-    float mx = fmaxf(fmaxf(s[0][0][0], s[0][0][1]), s[0][0][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[0][0][r]), s[0][0][r + 1]);
-    mx = swap32_max(fmaxf(mx, s[0][0][15]));
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    mx = fmaxf(fmaxf(mx, s[0][3]), s[1][0]);
+    mx = fmaxf(fmaxf(mx, s[1][1]), s[1][2]);
+    mx = swap32_max(swap16_max(fmaxf(mx, s[1][3])));
     *xf_mine = mx;
     block_barrier();
-    const float m_new = fmaxf(m_run[0], fmaxf(mx, *xf_other) * c_log2);
-    alpha[0] = __builtin_amdgcn_exp2f(m_run[0] - m_new);
-    m_run[0] = m_new;
-    float ps[1][4];
-    softmax_exp<32, 1, 0>(s, c_log2, m_run, ps);
-    bf16x8 pb[1][2];
-    softmax_pack<32, 1>(s, pb);
-    softmax_sum<1>(l_run, alpha, ps);
-    *(LDS_AS bf16x8*)(xp_mine) = pb[0][0];
-    *(LDS_AS bf16x8*)(xp_mine + 64 * 16) = pb[0][1];
+    const float m_new = fmaxf(m_run, fmaxf(mx, *xf_other) * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][i], c_log2, -m_new));
+    l_run = __builtin_fmaf(l_run, alpha, ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                                             ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+    bf16x8 pt[2];
+    pt[0] = __builtin_convertvector((f32x8{p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]}),
+                                    bf16x8);
+    *(LDS_AS bf16x8*)(xp_mine) = pt[0];
     block_barrier();
-    // P^T of this wave's key tile (rows 32 half ..) and of the partner's
-    // (rows 32 (half ^ 1) ..): own tile first, so that every operand index is
-    // a compile-time constant
-    bf16x8 pt[2][2];
-    pt[0][0] = pb[0][0];
-    pt[0][1] = pb[0][1];
-    pt[1][0] = *(LDS_AS const bf16x8*)(xp_other);
-    pt[1][1] = *(LDS_AS const bf16x8*)(xp_other + 64 * 16);
-    rescale_block<256, 1>(o, alpha);
-    // PV step i = 16 kt + 8 p + t: O^T tile t += V^T(key tile kt, rows 16p..) P^T;
-    // the transposed reads run kMlaPfPV steps ahead, and copies 9-17 of the
-    // next block go out at steps 1, 5, .., 29 and 31
+    // P^T of this wave's key half, then of the partner's: own half first, so
+    // that the partner's read has landed by the time it is needed
+    pt[1] = *(LDS_AS const bf16x8*)(xp_other);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[t] *= alpha;
+    }
+    // PV step i = 16 kt + t: O^T tile t += V^T(key half kt) P^T(kt); the
+    // transposed reads run kMlaPfPV steps ahead
     auto tr_read = [&](int i, i16x4& a0, i16x4& a1) {
-      const int kt = i >> 4, p = (i >> 3) & 1, t = i & 7;
-      const int base = 128 * (t >> 1) + (kt ? vrow_other : vrow_mine) + (16 * p) * kMlaRow;
-      a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][0]));
-      a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(Ks + base + to[t & 1][1]));
+      const int kt = i >> 4, t = i & 15;
+      const char* base = Vs + (kt ? vrow_other : vrow_mine) + 128 * (t >> 2) + vo[t & 3];
+      a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base));
+      a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + 16 * kMlaRow));
     };
     i16x4 va[kMlaPfPV][2];
 #pragma unroll
     for (int i = 0; i < kMlaPfPV; ++i) tr_read(i, va[i][0], va[i][1]);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const int kt = i >> 4, p = (i >> 3) & 1, t = i & 7;
       const bf16x8 a =
           __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[i % kMlaPfPV][0], va[i % kMlaPfPV][1], 0, 1, 2, 3, 4,
                                                              5, 6, 7));
-      o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pt[kt][p], o[0][t], 0, 0, 0);
+      o[i & 15] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pt[i >> 4], o[i & 15], 0, 0, 0);
       if (i + kMlaPfPV < 32) tr_read(i + kMlaPfPV, va[i % kMlaPfPV][0], va[i % kMlaPfPV][1]);
-      if ((i & 3) == 1 || i == 31) mla_copy_one(rnext, i == 31 ? 17 : 9 + (i >> 2), cdst, wave, lane);
+      if ((i & 7) == 1 && i < 16) mla_copy_one(rnext, kMlaSCopies + (i >> 3), cdst, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     // issued after every copy of the next block, so that at the top of the
@@ -264,29 +294,25 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(const uint16_t* __r
     mla_touch_block(kvb, min(j + 2, b1 - 1) * kMlaBN, N, dummy, wave, lane);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
-  // the row sum: this wave's keys, then the partner's (same alpha sequence)
-  const float l_mine = swap32_sum(l_run[0]);
-  block_barrier();  // the partner has read this wave's last max
+  // the row sum: this wave's keys (over its four lane groups), then the
+  // partner's (same alpha sequence)
+  const float l_mine = swap32_sum(swap16_sum(l_run));
+  block_barrier();  // the partner has read this wave's last max; every wave is done with the ring
   *xf_mine = l_mine;
   block_barrier();
   const float l_tot = l_mine + *xf_other;
   const float inv = 1.0f / l_tot;
   // O^T (lane = head, registers = dims) goes through LDS so that each store
   // writes one head's 256 dims (1 KiB) contiguously: [head][dim] per wave,
-  // 16-byte chunk k of row h at k ^ (h & 15) (conflict-free both ways)
-  char* st = smem + wave * (32 * 1024);
+  // 16-byte chunk k of head h at k ^ h (conflict-free both ways)
+  char* st = smem + wave * (16 * 1024);
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *(LDS_AS f32x4*)(st + lq * 1024 + (((8 * t + 2 * g + hl) ^ (lq & 15)) << 4)) =
-          f32x4{o[0][t][4 * g] * inv, o[0][t][4 * g + 1] * inv, o[0][t][4 * g + 2] * inv, o[0][t][4 * g + 3] * inv};
+  for (int t = 0; t < 16; ++t) *(LDS_AS f32x4*)(st + s16 * 1024 + (((4 * t + g) ^ s16) << 4)) = o[t] * inv;
   // (a wave reads back only its own rows; its LDS accesses complete in order)
-  float* obase = ws_o + ((size_t)c * rows + (size_t)b * H + h0) * kMlaDv + 256 * half;
 #pragma unroll 4
-  for (int h = 0; h < 32; ++h)
-    *(f32x4*)(obase + (size_t)h * kMlaDv + 4 * lane) = *(LDS_AS const f32x4*)(st + h * 1024 + ((lane ^ (h & 15)) << 4));
-  if (half == 0 && hl == 0) ws_lse[(size_t)c * rows + row] = kLn2 * (m_run[0] + __builtin_amdgcn_logf(l_tot));
+  for (int h = 0; h < 16; ++h)
+    *(f32x4*)(obase + (size_t)h * kMlaDv + 4 * lane) = *(LDS_AS const f32x4*)(st + h * 1024 + ((lane ^ h) << 4));
+  if (half == 0 && g == 0) ws_lse[(size_t)c * rows + row] = kLn2 * (m_run + __builtin_amdgcn_logf(l_tot));
 }
 
 // Merge of the NC chunk partials of one (b, h) row, for NC <= kMlaMergePF
@@ -456,7 +482,7 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   float* ws_o = (float*)workspace;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * kMlaDv;
   clear_last_hip_error();
-  hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)(p.groups * p.nc)), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)(p.groups * p.nc)), dim3(512), 0, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
                      scale_args(scale).q_mode);
   if (p.nc <= kMlaMergePF)
