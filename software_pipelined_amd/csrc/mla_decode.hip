@@ -42,7 +42,6 @@ constexpr int kMlaK = kMlaDk / 32;                 // 32-wide contraction steps 
 constexpr int kMlaST = 2;                          // ring slots: one block in flight behind the one in use
 constexpr int kMlaXP = 64 * 16;                    // P^T exchange: one bf16x8 per lane
 constexpr int kMlaXchg = kMlaWaves * (kMlaXP + 64 * 4);  // per wave: P^T, and one float per lane (max, then l)
-constexpr int kMlaDummy = kMlaWaves * 256;         // L2-prefetch landing words, one per lane
 constexpr int kMlaSCopies = 7;                     // of a wave's 9 copies, those issued in the S stream
 // fragment reads in flight ahead of the MFMAs (a PV step takes two
 // transposed reads)
@@ -86,26 +85,6 @@ __device__ __forceinline__ void mla_copy_block(const uint16_t* kvb, int row0, in
   for (int t = 0; t < kMlaCpw; ++t) mla_copy_one(r, t, dst, wave, lane);
 }
 
-// L2 prefetch of a block: one 4-byte read per 64-byte line of its rows, each
-// landing in a throwaway LDS word of the wave (an LDS-bound load, so it ties
-// up no register). With one block in flight in the LDS ring, the copy of the
-// next block then finds its lines in L2 instead of waiting on HBM.
-constexpr int kMlaTouch = (kMlaBlock / 64 + 64 * kMlaWaves - 1) / (64 * kMlaWaves);  // reads per wave per block (3)
-__device__ __forceinline__ void mla_touch_block(const uint16_t* kvb, int row0, int N, char* dummy, int wave,
-                                                int lane) {
-  const int rows = __builtin_amdgcn_readfirstlane(min(N - row0, kMlaBN));
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(kvb + (size_t)row0 * kMlaDk), (short)0,
-                                                                     rows * kMlaRow, kRsrcWord3);
-  const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void*)dummy;
-#pragma unroll
-  for (int t = 0; t < kMlaTouch; ++t) {
-    const int voff = ((t * kMlaWaves + wave) * 64 + lane) * 64;  // past the block: the range check reads nothing
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
-                 "s"(m0)
-                 : "m0", "memory");
-  }
-}
-
 // max and sum over lanes l and l ^ 16 (v_permlane16_swap exchanges the odd
 // 16-lane rows of one copy with the even rows of the other)
 __device__ __forceinline__ float swap16_max(float x) {
@@ -124,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
                                                             int N, int H, int nc, float c_log2, int q_mode) {
   static_assert(kMlaCopies % kMlaWaves == 0, "copies split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg + kMlaDummy];
+  __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg];
   const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = wave >> 1, half = wave & 1;
@@ -153,7 +132,6 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
   const char* xp_other = xbase + (wave ^ 1) * kMlaXP + lane * 16;
   float* xf_mine = (float*)(xbase + kMlaWaves * kMlaXP) + wave * 64 + lane;
   const float* xf_other = (const float*)(xbase + kMlaWaves * kMlaXP) + (wave ^ 1) * 64 + lane;
-  char* dummy = xbase + kMlaXchg + wave * 256;
   // row fragments (K and Q): row 16m + s16, chunk 4kk + g at
   // 128 (kk >> 1) + 16 ((4 (kk & 1) + g) ^ f(s16))
   const int fk = mla_swz(s16);
@@ -175,13 +153,13 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
 
   // The 64 heads' Q rows are contiguous: they go to ring slot 1 as a 64-row
   // block (same layout) while block b0 goes to slot 0. Each iteration then
-  // issues the next block's copies, and the L2 prefetch of the block after
-  // (past the chunk end: duplicates of its last block, so the count of
-  // younger loads at the top of a block is always kMlaTouch).
+  // issues the copies of the next block (past the chunk end: a duplicate of
+  // its last block). There is no L2 prefetch of the block after: a
+  // one-read-per-line touch of it, which paid off with four waves per
+  // workgroup, slows this kernel down.
   mla_copy_block(Q + ((size_t)b * H + hgi * 64) * kMlaDk, 0, kMlaBN, smem + kMlaBlock, wave, lane);
   mla_copy_block(kvb, b0 * kMlaBN, N, smem, wave, lane);
-  mla_touch_block(kvb, min(b0 + 1, b1 - 1) * kMlaBN, N, dummy, wave, lane);
-  wait_vmcnt<kMlaCpw + kMlaTouch>();  // the Q copies, issued first, have landed
+  wait_vmcnt<kMlaCpw>();  // the Q copies, issued first, have landed
   block_barrier();
   // Q^T fragments (B operand): lane holds q[head h0 + s16][32 kk + 8g .. +7],
   // row 16 tile + s16 of the Q image; slot 1 is refilled only after the
@@ -198,7 +176,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
   }
   for (int j = b0; j < b1; ++j) {
     const int slot = (j - b0) & 1;
-    wait_vmcnt<kMlaTouch>();
+    wait_vmcnt<0>();
     block_barrier();
     // the next block's 9 copies are spread over this block's MFMA streams: 7
     // in the S stream (one per 5 MFMAs), the last 2 early in the PV stream, so
@@ -289,9 +267,6 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
       if ((i & 7) == 1 && i < 16) mla_copy_one(rnext, kMlaSCopies + (i >> 3), cdst, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // issued after every copy of the next block, so that at the top of the
-    // next block only these kMlaTouch reads may still be in flight
-    mla_touch_block(kvb, min(j + 2, b1 - 1) * kMlaBN, N, dummy, wave, lane);
   }
   wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   // the row sum: this wave's keys (over its four lane groups), then the
