@@ -45,6 +45,9 @@ SHAPES = [
     (2, 128, 100),
     (1, 128, 1000),    # several blocks per chunk, ragged tail
     (3, 64, 2049),
+    (2, 192, 500),     # three 64-head workgroups per (sequence, chunk)
+    (1, 256, 700),     # four
+    (300, 64, 128),    # one chunk per sequence (the whole cache), more workgroups than CUs
 ]
 
 
