@@ -395,8 +395,8 @@ __global__ __launch_bounds__(256, 1) void mla_combine_wide(const float* __restri
 
 // MLA decoding: H a multiple of 64 (64 heads per workgroup); chunks sized so
 // that one resident round of workgroups (one per CU) covers the cache, at
-// least two 64-row blocks per chunk (one-block chunks: B = 1 took 26.7
-// against 22.5 us, the per-workgroup Q load and partial stores then
+// least two 64-row blocks per chunk (one-block chunks: B = 1 took 24.7
+// against 20.6 us, the per-workgroup Q load and partial stores then
 // dominate).
 struct MlaPlan {
   int nc;
