@@ -31,18 +31,36 @@ namespace {
 // which become contraction indices 8g + i and 8g + 4 + i of the 32-key step;
 // the V^T operand reads its rows in that same order (two transposed reads,
 // rows 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3).
+//
+// With few sequences the same kernel runs on workgroups of one head tile
+// (16 heads, two waves; MlaShape<1>), so that the grid still covers the CUs.
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 constexpr int kMlaDk = 576, kMlaDv = 512, kMlaBN = 64;
-constexpr int kMlaWaves = 8;
 constexpr int kMlaRow = kMlaDk * 2;                // bytes per cache row
 constexpr int kMlaBlock = kMlaBN * kMlaRow;        // 72 KiB per 64-row block
 constexpr int kMlaCopies = kMlaBlock / 1024;       // 1 KiB copies per block
-constexpr int kMlaCpw = kMlaCopies / kMlaWaves;    // copies per wave and block (9)
 constexpr int kMlaK = kMlaDk / 32;                 // 32-wide contraction steps (18)
 constexpr int kMlaST = 2;                          // ring slots: one block in flight behind the one in use
 constexpr int kMlaXP = 64 * 16;                    // P^T exchange: one bf16x8 per lane
-constexpr int kMlaXchg = kMlaWaves * (kMlaXP + 64 * 4);  // per wave: P^T, and one float per lane (max, then l)
-constexpr int kMlaSCopies = 7;                     // of a wave's 9 copies, those issued in the S stream
+
+// A workgroup of T head tiles (16 heads each) and 2T waves: T = 4 (64 heads,
+// eight waves, two per SIMD) by default; T = 1 (16 heads, two waves) when
+// 64-head workgroups would leave CUs idle (few sequences: B = 1 fills 64 of
+// 256 CUs with them, all 256 with 16-head ones).
+template <int T>
+struct MlaShape {
+  static constexpr int W = 2 * T;                        // waves
+  static constexpr int HEADS = 16 * T;
+  static constexpr int CPW = kMlaCopies / W;             // 1 KiB copies per wave and block (9 or 36)
+  static constexpr int SC = T == 4 ? 7 : CPW;            // of them, issued in the S stream
+  static constexpr int XCHG = W * (kMlaXP + 64 * 4);     // per wave: P^T, and one float per lane (max, then l)
+  // the copy issued at S-stream step i (of 36) and at PV-stream step i (of
+  // 32), or -1: with T = 4 one per five S steps and the last two early in
+  // the PV stream; with T = 1 one per S step
+  static constexpr int s_copy(int i) { return T == 4 ? (i % 5 == 1 ? i / 5 : -1) : (i < CPW ? i : -1); }
+  static constexpr int pv_copy(int i) { return T == 4 && (i & 7) == 1 && i < 16 ? SC + (i >> 3) : -1; }
+  static_assert(kMlaCopies % W == 0, "copies split evenly over the waves");
+};
 // fragment reads in flight ahead of the MFMAs (a PV step takes two
 // transposed reads)
 constexpr int kMlaPfQK = 6, kMlaPfPV = 8;
@@ -66,23 +84,26 @@ __device__ __forceinline__ int mla_swz(int row) {
 __device__ __forceinline__ int mla_phys(int c, int row) { return c ^ mla_swz(row); }
 
 // A block's rows [row0, min(row0 + 64, N)) as a buffer resource (reads past
-// them return zeros), and copy t (of 9 per wave) of the block into an LDS
-// image: 1 KiB per copy, lane l's 16 bytes at dst + 1024 (8t + wave) + 16 l.
+// them return zeros), and copy t (of 72 / W per wave, W waves) of the block
+// into an LDS image: 1 KiB per copy, lane l's 16 bytes at dst + 1024 (W t +
+// wave) + 16 l.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mla_rsrc(const uint16_t* kvb, int row0, int N) {
   const int rows = __builtin_amdgcn_readfirstlane(min(N - row0, kMlaBN));
   return __builtin_amdgcn_make_buffer_rsrc((void*)(kvb + (size_t)row0 * kMlaDk), (short)0, rows * kMlaRow,
                                            kRsrcWord3);
 }
+template <int W>
 __device__ __forceinline__ void mla_copy_one(__amdgpu_buffer_rsrc_t r, int t, char* dst, int wave, int lane) {
-  const int idx = t * kMlaWaves + wave;
+  const int idx = t * W + wave;
   const int pidx = idx * 64 + lane;
   const int row = pidx / 72, pc = pidx % 72;
   cs_dma(r, row * kMlaRow + (mla_phys(pc, row) << 4), dst + idx * 1024);
 }
+template <int W>
 __device__ __forceinline__ void mla_copy_block(const uint16_t* kvb, int row0, int N, char* dst, int wave, int lane) {
   const __amdgpu_buffer_rsrc_t r = mla_rsrc(kvb, row0, N);
 #pragma unroll
-  for (int t = 0; t < kMlaCpw; ++t) mla_copy_one(r, t, dst, wave, lane);
+  for (int t = 0; t < kMlaCopies / W; ++t) mla_copy_one<W>(r, t, dst, wave, lane);
 }
 
 // max and sum over lanes l and l ^ 16 (v_permlane16_swap exchanges the odd
@@ -96,24 +117,26 @@ __device__ __forceinline__ float swap16_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Grid: B * (H/64) * NC workgroups of 512 threads. Chunk c of the key blocks
-// as chunk_begin.
-__global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
+// Grid: B * (H/16T) * NC workgroups of 128T threads. Chunk c of the key
+// blocks as chunk_begin.
+template <int T>
+__global__ __launch_bounds__(128 * T, 1) void mla_decode_partial(const uint16_t* __restrict__ Q,
                                                             const uint16_t* __restrict__ KV,
                                                             float* __restrict__ ws_o, float* __restrict__ ws_lse,
                                                             int N, int H, int nc, float c_log2, int q_mode) {
-  static_assert(kMlaCopies % kMlaWaves == 0, "copies split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + kMlaXchg];
+  using S = MlaShape<T>;
+  constexpr int W = S::W;
+  __shared__ __attribute__((aligned(1024))) char smem[kMlaST * kMlaBlock + S::XCHG];
   const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = wave >> 1, half = wave & 1;
-  // The H/64 head groups of one (sequence, chunk) take consecutive logical
-  // ids, which xcd_remap places on one XCD at once: the group that fetches a
-  // cache block second finds it in that XCD's L2.
-  const int hg = H / 64;
+  // The H/16T head groups of one (sequence, chunk) take consecutive logical
+  // ids, which xcd_remap places on one XCD at once: the groups that fetch a
+  // cache block after the first find it in that XCD's L2.
+  const int hg = H / S::HEADS;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hgi = L % hg, bc = L / hg;
-  const int b = bc / nc, c = bc % nc, h0 = hgi * 64 + 16 * tile;
+  const int b = bc / nc, c = bc % nc, h0 = hgi * S::HEADS + 16 * tile;
   const int nblk = (N + kMlaBN - 1) / kMlaBN;
   const int b0 = chunk_begin(c, nblk, nc), b1 = chunk_begin(c + 1, nblk, nc);
   const uint16_t* kvb = KV + (size_t)b * N * kMlaDk;
@@ -130,8 +153,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
   char* xbase = smem + kMlaST * kMlaBlock;
   char* xp_mine = xbase + wave * kMlaXP + lane * 16;
   const char* xp_other = xbase + (wave ^ 1) * kMlaXP + lane * 16;
-  float* xf_mine = (float*)(xbase + kMlaWaves * kMlaXP) + wave * 64 + lane;
-  const float* xf_other = (const float*)(xbase + kMlaWaves * kMlaXP) + (wave ^ 1) * 64 + lane;
+  float* xf_mine = (float*)(xbase + W * kMlaXP) + wave * 64 + lane;
+  const float* xf_other = (const float*)(xbase + W * kMlaXP) + (wave ^ 1) * 64 + lane;
   // row fragments (K and Q): row 16m + s16, chunk 4kk + g at
   // 128 (kk >> 1) + 16 ((4 (kk & 1) + g) ^ f(s16))
   const int fk = mla_swz(s16);
@@ -151,15 +174,15 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
   for (int t = 0; t < 16; ++t) o[t] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // The 64 heads' Q rows are contiguous: they go to ring slot 1 as a 64-row
-  // block (same layout) while block b0 goes to slot 0. Each iteration then
+  // The workgroup's Q rows (16T heads, contiguous) go to ring slot 1 as a
+  // 16T-row block (same layout) while block b0 goes to slot 0. Each iteration then
   // issues the copies of the next block (past the chunk end: a duplicate of
   // its last block). There is no L2 prefetch of the block after: a
   // one-read-per-line touch of it, which paid off with four waves per
   // workgroup, slows this kernel down.
-  mla_copy_block(Q + ((size_t)b * H + hgi * 64) * kMlaDk, 0, kMlaBN, smem + kMlaBlock, wave, lane);
-  mla_copy_block(kvb, b0 * kMlaBN, N, smem, wave, lane);
-  wait_vmcnt<kMlaCpw>();  // the Q copies, issued first, have landed
+  mla_copy_block<W>(Q + ((size_t)b * H + hgi * S::HEADS) * kMlaDk, 0, S::HEADS, smem + kMlaBlock, wave, lane);
+  mla_copy_block<W>(kvb, b0 * kMlaBN, N, smem, wave, lane);
+  wait_vmcnt<S::CPW>();  // the Q copies, issued first, have landed
   block_barrier();
   // Q^T fragments (B operand): lane holds q[head h0 + s16][32 kk + 8g .. +7],
   // row 16 tile + s16 of the Q image; slot 1 is refilled only after the
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
       for (int i = 0; i < 2 * kMlaK; ++i) {
         s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[i % kMlaPfQK], qf[0][i >> 1], s[i & 1], 0, 0, 0);
         if (i + kMlaPfQK < 2 * kMlaK) kf[i % kMlaPfQK] = kread(i + kMlaPfQK);
-        if (i % 5 == 1) mla_copy_one(rnext, i / 5, cdst, wave, lane);
+        if (S::s_copy(i) >= 0) mla_copy_one<W>(rnext, S::s_copy(i), cdst, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kv0 + 32 > N) {
@@ -212,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < kMlaSCopies; ++t) mla_copy_one(rnext, t, cdst, wave, lane);
+      for (int t = 0; t < S::SC; ++t) mla_copy_one<W>(rnext, t, cdst, wave, lane);
 #pragma unroll
       for (int m = 0; m < 2; ++m) s[m] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_partial(const uint16_t* __r
                                                              5, 6, 7));
       o[i & 15] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pt[i >> 4], o[i & 15], 0, 0, 0);
       if (i + kMlaPfPV < 32) tr_read(i + kMlaPfPV, va[i % kMlaPfPV][0], va[i % kMlaPfPV][1]);
-      if ((i & 7) == 1 && i < 16) mla_copy_one(rnext, kMlaSCopies + (i >> 3), cdst, wave, lane);
+      if (S::pv_copy(i) >= 0) mla_copy_one<W>(rnext, S::pv_copy(i), cdst, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -393,13 +416,14 @@ __global__ __launch_bounds__(256, 1) void mla_combine_wide(const float* __restri
 }
 
 
-// MLA decoding: H a multiple of 64 (64 heads per workgroup); chunks sized so
+// MLA decoding: H a multiple of 64 (64 heads per workgroup, or 16 when that
+// leaves CUs idle); chunks sized so
 // that one resident round of workgroups (one per CU) covers the cache, at
 // least two 64-row blocks per chunk (one-block chunks: B = 1 took 24.7
 // against 20.6 us, the per-workgroup Q load and partial stores then
 // dominate).
 struct MlaPlan {
-  int nc;
+  int nc, tiles;  // key chunks; 16-head tiles per workgroup (4 or 1)
   long long groups, rows;
   size_t ws_bytes;  // nc * rows * (Dv + 1) floats
 };
@@ -409,6 +433,7 @@ int mla_plan(int B, int H, int N, MlaPlan* p) {
   if (H % 64 != 0) return ATTN_ERR_BAD_SHAPE;
   p->rows = (long long)B * H;
   p->groups = (long long)B * (H / 64);
+  p->tiles = 4;
   p->nc = 0;
   p->ws_bytes = 0;
   if (p->rows == 0) return ATTN_OK;
@@ -418,9 +443,17 @@ int mla_plan(int B, int H, int N, MlaPlan* p) {
       p->rows > INT_MAX)
     return ATTN_ERR_BAD_SHAPE;
   const long long nblk = (N + kMlaBN - 1) / kMlaBN;
-  long long nc = (256 + p->groups - 1) / p->groups;  // one resident round (one workgroup per CU)
-  nc = std::min(nc, std::max(1LL, nblk / 2));  // at least two blocks per chunk
-  nc = std::min(nc, (long long)kDecodeMaxChunks);
+  auto chunks = [nblk](long long groups) {
+    long long n = (256 + groups - 1) / groups;  // one resident round (one workgroup per CU)
+    n = std::min(n, std::max(1LL, nblk / 2));   // at least two blocks per chunk
+    return std::min(n, (long long)kDecodeMaxChunks);
+  };
+  long long nc = chunks(p->groups);
+  if (p->groups * nc < 256) {  // 64-head workgroups would leave CUs idle: 16-head ones
+    p->tiles = 1;
+    p->groups = (long long)B * (H / 16);
+    nc = chunks(p->groups);
+  }
   long long floats = 0;
   if (__builtin_mul_overflow(nc * p->rows, (long long)(kMlaDv + 1), &floats) || floats > (1LL << 40) ||
       !grid_fits(p->groups * nc, 256) || !grid_fits(p->rows, 256))
@@ -457,9 +490,15 @@ int mla_decode(const void* q, const void* kv, float* out, float* lse, int B, int
   float* ws_o = (float*)workspace;
   float* ws_lse = ws_o + (size_t)p.nc * p.rows * kMlaDv;
   clear_last_hip_error();
-  hipLaunchKernelGGL(mla_decode_partial, dim3((unsigned)(p.groups * p.nc)), dim3(512), 0, (hipStream_t)stream,
-                     (const uint16_t*)q, (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
-                     scale_args(scale).q_mode);
+  const dim3 grid((unsigned)(p.groups * p.nc));
+  if (p.tiles == 4)
+    hipLaunchKernelGGL(mla_decode_partial<4>, grid, dim3(512), 0, (hipStream_t)stream, (const uint16_t*)q,
+                       (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
+                       scale_args(scale).q_mode);
+  else
+    hipLaunchKernelGGL(mla_decode_partial<1>, grid, dim3(128), 0, (hipStream_t)stream, (const uint16_t*)q,
+                       (const uint16_t*)kv, ws_o, ws_lse, N, H, p.nc, scale_args(scale).c_log2,
+                       scale_args(scale).q_mode);
   if (p.nc <= kMlaMergePF)
     hipLaunchKernelGGL(mla_combine, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
                        (const float*)ws_o, (const float*)ws_lse, out, lse, (int)p.rows, p.nc);

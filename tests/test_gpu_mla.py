@@ -48,6 +48,9 @@ SHAPES = [
     (2, 192, 500),     # three 64-head workgroups per (sequence, chunk)
     (1, 256, 700),     # four
     (300, 64, 128),    # one chunk per sequence (the whole cache), more workgroups than CUs
+    # enough sequences for 64-head workgroups (fewer take 16-head ones), with ragged tails
+    (64, 128, 1000),
+    (128, 64, 2049),   # the last block's second half holds no key
 ]
 
 
