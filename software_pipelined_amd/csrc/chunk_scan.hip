@@ -212,7 +212,10 @@ __global__ __launch_bounds__(NW * 64, HT == 2 ? 4 : 5) void chunk_scan_fwd(const
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int mm = mw + 4 * i + (lane >> 4);
-      if (mm < Lc) *(f32x4*)(OUT + (((size_t)b * S + c0 + mm) * H + h + hh) * kCsP + 4 * cl) = v[i];
+      // streaming stores: the output is written once and never read back
+      // here (2 % faster than plain stores)
+      if (mm < Lc)
+        __builtin_nontemporal_store(v[i], (f32x4*)(OUT + (((size_t)b * S + c0 + mm) * H + h + hh) * kCsP + 4 * cl));
     }
   }
 }
