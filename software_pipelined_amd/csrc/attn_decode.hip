@@ -52,6 +52,12 @@ __device__ __forceinline__ void copy_block_wave(const uint16_t* Kh, const uint16
 }
 
 
+// Ring slots per wave: three at d = 128 (two blocks in flight behind the one
+// being multiplied, three waves per CU: 1-6 % faster than two slots and four
+// waves once the copies stream), two otherwise (at d = 256 three slots would
+// leave one wave per CU).
+constexpr int decode_slots(int d) { return d == 128 ? 3 : 2; }
+
 // Grid: (B*H*n_qt) x (NC / NW) workgroups of NW waves; wave w of workgroup
 // (x, y) takes chunk y*NW + w of query tile x % n_qt of head x / n_qt.
 template <int D, int NW, int BN>
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int BH, int Nq, int Nkv, int n_qt, int nc,
     float c_log2, int q_mode) {
-  constexpr int ST = 2;
+  constexpr int ST = decode_slots(D);
   constexpr int MAT = BN * D * 2;
   constexpr int PER_BLOCK = 2 * Tile<D, 1, BN>::LOADS;
   __shared__ __attribute__((aligned(1024))) char smem[NW * ST * 2 * MAT];
@@ -93,13 +99,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_decode_partial(
     }
     return;
   }
-  copy_block_wave<D, BN>(Kh, Vh, b0 * BN, Nkv, ks(0), vs(0), lane);
+  // blocks b0 .. b0 + ST - 2 go out first; iteration j refills the slot of
+  // block j - 1 with block j + ST - 1 and waits for block j only
+#pragma unroll
+  for (int i = 0; i < ST - 1; ++i)
+    if (b0 + i < b1) copy_block_wave<D, BN>(Kh, Vh, (b0 + i) * BN, Nkv, ks(i), vs(i), lane);
   for (int j = b0; j < b1; ++j) {
-    const int slot = (j - b0) & 1;
+    const int slot = (j - b0) % ST;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the slot about to be refilled are done
-    if (j + 1 < b1) {
-      copy_block_wave<D, BN>(Kh, Vh, (j + 1) * BN, Nkv, ks(slot ^ 1), vs(slot ^ 1), lane);
-      wait_vmcnt<PER_BLOCK>();  // block j has landed, block j+1 may stay in flight
+    if (j + ST - 1 < b1) {
+      const int ns = (j + ST - 1 - b0) % ST;
+      copy_block_wave<D, BN>(Kh, Vh, (j + ST - 1) * BN, Nkv, ks(ns), vs(ns), lane);
+      wait_vmcnt<(ST - 1) * PER_BLOCK>();  // block j has landed, the later ones may stay in flight
+    } else if (ST == 3 && j + 1 < b1) {
+      wait_vmcnt<PER_BLOCK>();
     } else {
       wait_vmcnt<0>();
     }
@@ -202,20 +215,21 @@ __global__ __launch_bounds__(256, 1) void attn_decode_combine(const float* __res
   if (tid == 0) LSE[row] = mx + kLn2 * __builtin_amdgcn_logf(wsum);
 }
 
-// Split-KV decoding: 32-key blocks, 4 waves per workgroup (2 at d = 256,
-// whose 64 KiB ring per wave fills the LDS). Each wave's K/V ring holds
-// 2 slots x 2 matrices x 32 keys x d bf16, so the 160 KiB LDS of a CU keeps
-// 8 waves resident at d = 64, 4 at d = 128 and 2 at d = 256; the chunks are
-// sized so that one resident round of waves (256 CUs) streams the cache,
-// rounded up to a multiple of the waves per workgroup.
+// Split-KV decoding: 32-key blocks, 4 waves per workgroup at d = 64, 3 at
+// d = 128 and 2 at d = 256 (whose 64 KiB ring per wave fills the LDS). Each
+// wave's K/V ring holds decode_slots(d) slots x 2 matrices x 32 keys x d
+// bf16, so the 160 KiB LDS of a CU keeps 8 waves resident at d = 64, 3 at
+// d = 128 and 2 at d = 256; the chunks are sized so that one resident round
+// of waves (256 CUs) streams the cache, rounded up to a multiple of the waves
+// per workgroup.
 constexpr int kDecodeBN = 32;
 constexpr int kDecodeCUs = 256;
 constexpr int kDecodeLdsPerCU = 160 * 1024;
 
 constexpr int decode_waves(int d, int nw) {
-  return kDecodeCUs * (kDecodeLdsPerCU / (nw * 2 * 2 * kDecodeBN * d * 2)) * nw;
+  return kDecodeCUs * (kDecodeLdsPerCU / (nw * decode_slots(d) * 2 * kDecodeBN * d * 2)) * nw;
 }
-static_assert(decode_waves(64, 4) == 2048 && decode_waves(128, 4) == 1024 && decode_waves(256, 2) == 512,
+static_assert(decode_waves(64, 4) == 2048 && decode_waves(128, 3) == 768 && decode_waves(256, 2) == 512,
               "resident decode waves");
 static_assert(decode_waves(64, 4) <= kDecodeMaxChunks, "chunk bound of the merge");
 
@@ -236,7 +250,7 @@ int decode_plan(int B, int H, int Nq, int Nkv, int d, DecodePlan* p) {
       __builtin_mul_overflow(rows_kv, (long long)d, &elems_kv))
     return ATTN_ERR_BAD_SHAPE;
   p->rows = rows;
-  p->nw = d == 256 ? 2 : 4;
+  p->nw = d == 256 ? 2 : (d == 128 ? 3 : 4);
   p->n_qt = (Nq + 31) / 32;
   p->nc = 0;
   p->ws_bytes = 0;
@@ -321,7 +335,7 @@ hipError_t launch_decode_d(int d, const DecodePlan& p, const void* q, const void
                            float* lse, int BH, int Nq, int Nkv, float scale, void* ws, hipStream_t stream) {
   switch (d) {
     case 64: return launch_decode<64, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
-    case 128: return launch_decode<128, 4>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
+    case 128: return launch_decode<128, 3>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
     default: return launch_decode<256, 2>(p, q, k, v, out, lse, BH, Nq, Nkv, scale, ws, stream);
   }
 }
