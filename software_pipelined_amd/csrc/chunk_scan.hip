@@ -91,7 +91,8 @@ __device__ __forceinline__ void cs_copy_block(const uint16_t* xh, const uint16_t
 // the cb columns (copied and read once per block) and their x rows are
 // adjacent in memory.
 template <int NW, int HT>
-__global__ __launch_bounds__(NW * 64, HT == 2 ? 4 : 5) void chunk_scan_fwd(const uint16_t* __restrict__ X, const uint16_t* __restrict__ CB,
+__global__ __launch_bounds__(NW * 64, HT == 2 ? 4 : 5) void chunk_scan_fwd(const uint16_t* __restrict__ X,
+                                                                           const uint16_t* __restrict__ CB,
                                                          const float* __restrict__ DT, const float* __restrict__ DAC,
                                                          float* __restrict__ OUT, int S, int H, int L, int nc) {
   static_assert(NW == 4, "one 1 KiB copy per wave covers a quarter of a 32 x 64 bf16 block");
@@ -229,7 +230,8 @@ int chunk_scan_check(int B, int S, int H, int P, int L, long long* groups) {
   if (L < kCsBK || L > 256 || L % kCsBK != 0) return ATTN_ERR_BAD_SHAPE;
   long long rows = 0, elems = 0, g = 0;
   const long long nc = ((long long)S + L - 1) / L;
-  if (__builtin_mul_overflow((long long)B * S, (long long)H, &rows) || __builtin_mul_overflow(rows, (long long)P, &elems) ||
+  if (__builtin_mul_overflow((long long)B * S, (long long)H, &rows) ||
+      __builtin_mul_overflow(rows, (long long)P, &elems) ||
       elems > (1LL << 50) || __builtin_mul_overflow((long long)B * nc, (long long)H, &g) || g > INT_MAX ||
       (long long)H * P * 2 * kCsBK > INT_MAX)
     return ATTN_ERR_BAD_SHAPE;

@@ -314,13 +314,14 @@ __global__ __launch_bounds__(128 * T, 1) void mla_decode_partial(const uint16_t*
 }
 
 // Merge of the NC chunk partials of one (b, h) row, for NC <= kMlaMergePF
-// (many rows, few chunks): one wave per row, four rows per workgroup, lane l owning output dims 8l .. 8l + 7. Every lane reads
-// all NC chunk LSEs (the same addresses in every lane: one request each) and
-// its 8 dims of every partial, all issued before any weight is known, so the
-// merge costs one memory round trip; no barrier. (Few rows with many chunks
-// go to mla_combine_wide instead.) Weights and sums run over the
-// chunks in order: w_c = exp(LSE_c - max), O = sum w_c O_c / sum w_c,
-// LSE = max + ln(sum w_c) (an empty chunk has LSE -inf and weight 0).
+// (many rows, few chunks): one wave per row, four rows per workgroup, lane l
+// owning output dims 8l .. 8l + 7. Every lane reads all NC chunk LSEs (the
+// same addresses in every lane: one request each) and its 8 dims of every
+// partial, all issued before any weight is known, so the merge costs one
+// memory round trip; no barrier. (Few rows with many chunks go to
+// mla_combine_wide instead.) Weights and sums run over the chunks in order:
+// w_c = exp(LSE_c - max), O = sum w_c O_c / sum w_c, LSE = max + ln(sum w_c)
+// (an empty chunk has LSE -inf and weight 0).
 constexpr int kMlaMergePF = 8;  // chunks whose partials are loaded up front
 __global__ __launch_bounds__(256) void mla_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                    float* __restrict__ O, float* __restrict__ LSE, int rows, int nc) {
@@ -363,7 +364,8 @@ __global__ __launch_bounds__(256) void mla_combine(const float* __restrict__ ws_
 // Merge for many chunks (more than kMlaMergePF): one workgroup per row (as
 // attn_decode_combine), two output dims per thread, the chunk weights shared
 // through LDS.
-__global__ __launch_bounds__(256, 1) void mla_combine_wide(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+__global__ __launch_bounds__(256, 1) void mla_combine_wide(const float* __restrict__ ws_o,
+                                                          const float* __restrict__ ws_lse,
                                                      float* __restrict__ O, float* __restrict__ LSE, int rows, int nc) {
   __shared__ float w_sh[kDecodeMaxChunks];
   __shared__ float red[8];
