@@ -48,6 +48,7 @@ SHAPES = [
     (2, 2, 1, 64, 256),
     (1, 1, 3, 4095, 256),
     (3, 1, 32, 2049, 64),
+    (16, 16, 1, 200, 128),   # chunks of 2, 2 and 3 blocks (d = 128: three-slot rings), ragged tail
 ]
 
 
